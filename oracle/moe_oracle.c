@@ -83,14 +83,14 @@ int orc_validate_num_max(int64_t configured, int64_t derived)
     return 0;
 }
 
-/* The capacity relation with 4-token alignment of both capacities:
- * 0 <= T <= round_up4(ntpr) <= round_up4(nmax), nmax >= 1, ntpr >= 0.
+/* The capacity relation of [TT] "API design", with a positive maximum:
+ * 0 <= T <= ntpr <= nmax and nmax >= 1. Rounding both capacities up to a
+ * multiple of 4 ([NA] "Fix") keeps round_up4(ntpr) <= round_up4(nmax).
  * 0 when it holds, 1 otherwise. */
 int orc_check_capacity(int64_t T, int64_t ntpr, int64_t nmax)
 {
-    if (nmax < 1 || ntpr < 0 || T < 0) return 1;
-    if (T > orc_round_up4(ntpr)) return 1;
-    if (orc_round_up4(ntpr) > orc_round_up4(nmax)) return 1;
+    if (nmax < 1 || T < 0) return 1;
+    if (T > ntpr || ntpr > nmax) return 1;
     return 0;
 }
 

@@ -102,11 +102,17 @@ def test_capacity_relation_cases():
         ntpr = oracle.round_up4(max(a, b))
         assert oracle.check_capacity(a, ntpr, 4096) == 0
         assert oracle.check_capacity(b, ntpr, 4096) == 0
-    assert oracle.check_capacity(2047, 2047, 2048) == 0   # 2047 -> 2048 <= 2048
-    assert oracle.check_capacity(2048, 2047, 2048) == 0
-    assert oracle.check_capacity(2049, 2048, 4096) != 0   # T beyond capacity
-    assert oracle.check_capacity(0, 4097, 4096) != 0      # 4100 > 4096
+    assert oracle.check_capacity(2047, 2047, 2048) == 0
+    assert oracle.check_capacity(2048, 2047, 2048) != 0   # T above the capacity
+    assert oracle.check_capacity(2049, 2048, 4096) != 0
+    assert oracle.check_capacity(0, 4097, 4096) != 0      # capacity above the max
     assert oracle.check_capacity(0, 0, 0) != 0            # nmax must be >= 1
+    assert oracle.check_capacity(0, 0, 1) == 0            # T = 0 is a legal no-op
+    assert oracle.check_capacity(-1, 0, 1) != 0
+    # The relation implies the rounded capacities stay ordered.
+    for ntpr in range(0, 40):
+        for nmax in range(max(ntpr, 1), 40):
+            assert oracle.round_up4(ntpr) <= oracle.round_up4(nmax)
     lens = g["dynamic_lengths"]
     nmax = max(lens)
     for T in lens:
