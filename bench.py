@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE token layout -> dispatch -> combine hot path on one GPU.
+
+One step is one pass of the whole path over one synthetic batch already
+resident in HBM: moe_layout, moe_dispatch, the identity expert (the combine
+reads the dispatched buffer), moe_combine. The default workload is the
+DeepSeek-V3-shaped layer (T=4096, D=7168, E=256, top-8, bf16, Zipf(1.1)
+routing). Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsv3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "combine_moe_layout_05_amd", "csrc")
+KERNEL_SOURCES = {
+    "dispatch": ["dispatch.hip", "moe_kernels.h"],
+    "combine": ["combine.hip", "moe_kernels.h"],
+    "layout": ["layout.hip", "moe_kernels.h"],
+}
+METRIC = ("dispatch+combine tokens/s and achieved HBM GB/s (% of peak), "
+          "T=4096 D=7168 E=256 k=8")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dsv3")
+    p.add_argument("--cold-iters", type=int, default=10,
+                   help="iterations of the cache-flushed per-kernel measurement (0 = skip)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="budget of the oracle CPU baseline (0 = skip)")
+    p.add_argument("--dispatch-segments", type=int, default=0)
+    p.add_argument("--combine-segments", type=int, default=0)
+    p.add_argument("--nontemporal", type=int, default=-1,
+                   help="1/0 forces dispatch's streaming stores on/off; -1 keeps the default")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this size (for counter scaling)")
+    return p.parse_args()
+
+
+def bytes_per_token(w, kind: str) -> int:
+    """Algorithmic HBM bytes per token (every routed slot has an expert).
+    layout:   read ids (4K), write row_map (4K) and src_map (4K)
+    dispatch: read x row, row_map (4K), scores (4K); write K rows, s_e (4K)
+    combine:  read K rows, row_map (4K), scores (4K); write one row"""
+    eb = 2 if w.dtype == "bf16" else 4
+    row = w.D * eb
+    K = w.K
+    return {"layout": 12 * K,
+            "dispatch": row * (K + 1) + 12 * K,
+            "combine": row * (K + 1) + 8 * K}[kind]
+
+
+def source_digest(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload, or None when there is none or the kernel
+    source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kind}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != source_digest(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy(mib: int) -> None:
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": 5}), flush=True)
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); this path has no multi-GPU mode.", file=sys.stderr, flush=True)
+        return 2
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return 0
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from combine_moe_layout_05_amd import MoeDispatcher, load
+
+    load()                                   # fails loudly if the library is not built
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    w = workloads.WORKLOADS[args.workload]
+    log(f"workload {w.name}: T={w.T} D={w.D} E={w.E} K={w.K} {w.dtype} {w.routing}")
+    b = workloads.make_batch(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if w.dtype == "bf16":
+        x = torch.from_numpy(b["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(b["x"]).to(dev)
+    ids = torch.from_numpy(b["ids"]).to(dev)
+    s = torch.from_numpy(b["scores"]).to(dev)
+    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=dev)
+    if args.dispatch_segments or args.combine_segments or args.nontemporal >= 0:
+        cur = disp.get_tuning()
+        disp.set_tuning(args.dispatch_segments, args.combine_segments,
+                        bool(args.nontemporal) if args.nontemporal >= 0
+                        else cur["dispatch_nontemporal"])
+    tuning = disp.get_tuning()
+    ntpr = w.ntpr
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        lay = disp.layout(ids, ntpr)
+        if ev is not None:
+            ev[1].record()
+        disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
+        if ev is not None:
+            ev[2].record()
+        disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
+        if ev is not None:
+            ev[3].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    log(f"timed {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    lay_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dis_ms = [e[1].elapsed_time(e[2]) for e in events]
+    com_ms = [e[2].elapsed_time(e[3]) for e in events]
+    ms_per_step = elapsed * 1e3 / K
+    value = w.T * K / elapsed
+    avg = {"layout": float(np.mean(lay_ms)), "dispatch": float(np.mean(dis_ms)),
+           "combine": float(np.mean(com_ms))}
+    gbps = {k: bytes_per_token(w, k) * w.T / (avg[k] * 1e-3) / 1e9 for k in avg}
+    dc_ms = avg["dispatch"] + avg["combine"]
+    dc_bytes = (bytes_per_token(w, "dispatch") + bytes_per_token(w, "combine")) * w.T
+    log(f"step {ms_per_step * 1e3:.1f} us; layout {avg['layout'] * 1e3:.1f} us, "
+        f"dispatch {avg['dispatch'] * 1e3:.1f} us ({gbps['dispatch']:.0f} GB/s), "
+        f"combine {avg['combine'] * 1e3:.1f} us ({gbps['combine']:.0f} GB/s)")
+
+    # Cold-cache per-kernel times: a 1 GiB write evicts L2 and the MALL
+    # before each timed kernel (outside the timed interval).
+    cold = None
+    if args.cold_iters > 0:
+        log(f"cold-cache per-kernel timing, {args.cold_iters} iterations")
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cd, cc = [], []
+        for i in range(args.cold_iters):
+            lay = disp.layout(ids, ntpr)
+            scratch.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
+            e1.record()
+            scratch.fill_((i + 1) & 0xFF)
+            e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e2.record()
+            disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
+            e3.record()
+            torch.cuda.synchronize()
+            cd.append(e0.elapsed_time(e1))
+            cc.append(e2.elapsed_time(e3))
+        del scratch
+        cold = {"dispatch_us": float(np.median(cd)) * 1e3,
+                "combine_us": float(np.median(cc)) * 1e3}
+        cold["dispatch_gbps"] = bytes_per_token(w, "dispatch") * w.T / (cold["dispatch_us"] * 1e-6) / 1e9
+        cold["combine_gbps"] = bytes_per_token(w, "combine") * w.T / (cold["combine_us"] * 1e-6) / 1e9
+        log(f"cold: dispatch {cold['dispatch_us']:.1f} us, combine {cold['combine_us']:.1f} us")
+
+    dominant = "dispatch" if avg["dispatch"] >= avg["combine"] else "combine"
+    per_launch = bytes_per_token(w, dominant) * w.T
+    achieved = per_launch / (avg[dominant] * 1e-3) / 1e9
+    traffic = counter_traffic(dominant, w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": traffic, "kernel": dominant,
+                "algorithmic_bytes_per_launch": per_launch,
+                "avg_launch_us": round(avg[dominant] * 1e3, 2)}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"oracle CPU baseline on {cores} threads, ~{args.cpu_seconds:.0f} s")
+        n, t_start = 0, time.perf_counter()
+        while True:
+            oracle.run_pipeline(b["x"], b["ids"], b["scores"], w.T, ntpr, w.E, w.K,
+                                nthreads=cores)
+            n += 1
+            if time.perf_counter() - t_start >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - t_start
+        cpu = {"value": round(w.T * n / cpu_s, 1), "unit": "tokens/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{n} full {w.name} batches (T={w.T}) through the oracle's "
+                         f"layout+dispatch+combine, {cpu_s:.1f} s"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "K": w.K,
+                   "num_tokens_per_rank": w.ntpr, "num_max_tokens_per_rank": w.nmax,
+                   "routing": w.routing + (f"(s={w.zipf_s})" if w.routing == "zipf" else ""),
+                   "scores": w.scores, "parallelism": "single-gpu", "tuning": tuning},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "kernels_gbps": {k: round(v, 1) for k, v in gbps.items()},
+        "dispatch_combine": {
+            "us": round(dc_ms * 1e3, 2),
+            "tokens_per_s": round(w.T / (dc_ms * 1e-3), 1),
+            "gbps": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        },
+        "cold_cache": cold,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,73 @@
+"""Build libmoe_layout.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+    python combine_moe_layout_05_amd/build.py
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+if __package__:
+    from ._paths import LIB_PATH, PKG
+else:  # run as a script
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from _paths import LIB_PATH, PKG  # type: ignore
+
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+
+SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "moe_api.cpp"]
+HEADERS = [os.path.join(CSRC, "moe_kernels.h"), os.path.join(INCLUDE, "moe.h")]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # Packed fp32 vector ops stay off; the kernels never rely on them.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Every multiply-add in the combine is an explicit fmaf; nothing else
+    # is contracted, and fp32 denormals are kept (IEEE).
+    "-ffp-contract=off",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP library cannot be built")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into combine_moe_layout_05_amd/libmoe_layout.so."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB_PATH):
+        return True
+    t = os.path.getmtime(LIB_PATH)
+    return any(os.path.getmtime(p) > t for p in
+               [os.path.join(CSRC, s) for s in SOURCES] + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

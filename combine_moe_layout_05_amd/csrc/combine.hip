@@ -1,0 +1,192 @@
+// Combine gather-reduce on gfx950: for each token, the score-weighted sum of
+// the expert-output rows its slots were dispatched to, back in token order.
+//
+// What is computed ("fix(moe): equalize and align per-rank token counts for
+// HybridEP dispatch", sections "Fix" and "Testing": combine returns the
+// token-ordered output and slices the padding off; with identity experts a
+// token's output depends only on its own routing):
+//   y[t] = sum_{k=0..K-1, row_map[t][k] >= 0} scores[t][k] * y_e[row_map[t][k]]
+// in fp32, fused multiply-add in ascending k, starting from +0.0, stored in
+// the element type (bf16 rounds to nearest even; NaN becomes 0x7FC0). A slot
+// without an expert is skipped and its score is not read. Only t < T is
+// computed; padding rows are never materialized.
+//
+// Bound by HBM reads (K rows read per row written). One wavefront per
+// (token, row segment); per 16-byte chunk each lane issues the K row loads
+// back to back before any arithmetic, so K x U loads are in flight per lane.
+// No-expert slots load the token's first valid row instead (always written,
+// finite) and discard it, which keeps every load unconditional.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+typedef int32_t v4i __attribute__((ext_vector_type(4)));
+
+// bf16 <-> fp32 by bit manipulation: widening is exact; narrowing rounds to
+// nearest even, with every NaN mapped to the quiet NaN 0x7FC0.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <bool BF16>
+struct Lanes;
+
+template <>
+struct Lanes<false> {  // 4 fp32 per 16-byte chunk
+    static constexpr int N = 4;
+    __device__ static void fma_into(float (&acc)[N], float s, v4i v) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] = __builtin_fmaf(s, __int_as_float(v[i]), acc[i]);
+    }
+    __device__ static v4i pack(const float (&acc)[N]) {
+        v4i o;
+#pragma unroll
+        for (int i = 0; i < N; ++i) o[i] = __float_as_int(acc[i]);
+        return o;
+    }
+};
+
+template <>
+struct Lanes<true> {  // 8 bf16 per 16-byte chunk, element 2i in the low half
+    static constexpr int N = 8;
+    __device__ static void fma_into(float (&acc)[N], float s, v4i v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = static_cast<uint32_t>(v[i]);
+            acc[2 * i] = __builtin_fmaf(s, bf16_lo(w), acc[2 * i]);
+            acc[2 * i + 1] = __builtin_fmaf(s, bf16_hi(w), acc[2 * i + 1]);
+        }
+    }
+    __device__ static v4i pack(const float (&acc)[N]) {
+        v4i o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = static_cast<int32_t>(f32_to_bf16_bits(acc[2 * i]) |
+                                        (f32_to_bf16_bits(acc[2 * i + 1]) << 16));
+        return o;
+    }
+};
+
+template <int K, bool BF16, int U>
+__global__ __launch_bounds__(kMoveThreads)
+void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row_map,
+                    const float* __restrict__ scores, int32_t T, int32_t chunks,
+                    int32_t segments, int32_t seg_chunks, int64_t row_limit,
+                    v4i* __restrict__ y) {
+    using L = Lanes<BF16>;
+    __shared__ int32_t tile_rows[kMoveWaves * K];
+    __shared__ float tile_scores[kMoveWaves * K];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int64_t item0 = int64_t(blockIdx.x) * kMoveWaves;
+    const int64_t t_first = item0 / segments;
+    int64_t t_last = (item0 + kMoveWaves - 1) / segments;
+    if (t_last > int64_t(T) - 1) t_last = int64_t(T) - 1;
+    const int staged = static_cast<int>(t_last - t_first + 1) * K;
+    if (tid < staged) {
+        int32_t r = row_map[t_first * K + tid];
+        const bool ok = r >= 0 && r < row_limit;
+        tile_rows[tid] = ok ? r : -1;
+        tile_scores[tid] = ok ? scores[t_first * K + tid] : 0.0f;
+    }
+    __syncthreads();
+
+    const int64_t item = item0 + wave;
+    const int64_t t = item / segments;
+    if (t >= T) return;
+    const int seg = static_cast<int>(item - t * segments);
+    const int lt = static_cast<int>(t - t_first);
+
+    int32_t row[K];
+    float s[K];
+    int32_t fallback = -1;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        row[k] = __builtin_amdgcn_readfirstlane(tile_rows[lt * K + k]);
+        s[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tile_scores[lt * K + k])));
+        if (fallback < 0 && row[k] >= 0) fallback = row[k];
+    }
+
+    const int32_t c_begin = seg * seg_chunks;
+    const int32_t c_end = min(c_begin + seg_chunks, chunks);
+    v4i* dst = y + t * chunks;
+
+    if (fallback < 0) {  // no slot reaches an expert: +0.0
+        const v4i zero = {0, 0, 0, 0};
+        for (int32_t c = c_begin + lane; c < c_end; c += 64) dst[c] = zero;
+        return;
+    }
+
+    const v4i* src[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) src[k] = y_e + int64_t(row[k] >= 0 ? row[k] : fallback) * chunks;
+
+    for (int32_t c0 = c_begin; c0 < c_end; c0 += 64 * U) {
+        v4i v[U][K];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t c = min(c0 + u * 64 + lane, c_end - 1);
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[u][k] = src[k][c];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float acc[L::N];
+#pragma unroll
+            for (int i = 0; i < L::N; ++i) acc[i] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (row[k] >= 0) L::fma_into(acc, s[k], v[u][k]);
+            const int32_t c = c0 + u * 64 + lane;
+            if (c < c_end) dst[c] = L::pack(acc);
+        }
+    }
+}
+
+template <int K, bool BF16>
+hipError_t launch_k(const CombineArgs& a, int32_t segments, int32_t seg_chunks,
+                    hipStream_t stream) {
+    constexpr int U = K <= 4 ? 4 : 2;
+    const int64_t items = int64_t(a.T) * segments;
+    const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
+    hipLaunchKernelGGL((combine_kernel<K, BF16, U>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kMoveThreads), 0, stream, static_cast<const v4i*>(a.y_e),
+                       a.row_map, a.scores, a.T, a.chunks, segments, seg_chunks, a.row_limit,
+                       static_cast<v4i*>(a.y));
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_dtype(const CombineArgs& a, int32_t segments, int32_t seg_chunks,
+                        hipStream_t stream) {
+    switch (a.K) {
+#define MOE_COMBINE_CASE(k) \
+    case k: return launch_k<k, BF16>(a, segments, seg_chunks, stream);
+        MOE_COMBINE_CASE(1) MOE_COMBINE_CASE(2) MOE_COMBINE_CASE(3) MOE_COMBINE_CASE(4)
+        MOE_COMBINE_CASE(5) MOE_COMBINE_CASE(6) MOE_COMBINE_CASE(7) MOE_COMBINE_CASE(8)
+        MOE_COMBINE_CASE(9) MOE_COMBINE_CASE(10) MOE_COMBINE_CASE(11) MOE_COMBINE_CASE(12)
+        MOE_COMBINE_CASE(13) MOE_COMBINE_CASE(14) MOE_COMBINE_CASE(15) MOE_COMBINE_CASE(16)
+#undef MOE_COMBINE_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+    if (a.T <= 0) return hipSuccess;
+    const int32_t seg_chunks = segment_chunks(a.chunks, a.segments);
+    const int32_t segments = (a.chunks + seg_chunks - 1) / seg_chunks;
+    return a.bf16 ? launch_dtype<true>(a, segments, seg_chunks, stream)
+                  : launch_dtype<false>(a, segments, seg_chunks, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,307 @@
+// Host side of libmoe_layout.so: configuration checks, the capture-safe
+// buffer manager (one caller-owned workspace carved once into fixed-address
+// buffers) and the C ABI entry points declared in include/moe.h.
+//
+// Buffer lifetime follows "Unify expert parallel token dispatcher API",
+// section "API design": storage is sized once from the lifetime maximum
+// num_max_tokens_per_rank and never grows; each call only uses the current
+// capacity num_tokens_per_rank, so buffer addresses are stable across eager
+// calls and graph replays. Capacities are rounded up to a multiple of 4
+// tokens ("fix(moe): equalize and align per-rank token counts for HybridEP
+// dispatch", sections "Problem" and "Fix"). Per "ep: graph-safe worst-token
+// HT dispatch+combine" ("Internode" 1-3, "Intranode"), no entry point waits
+// on the device, reads anything back or shares host-visible state with
+// in-flight work: counts and the total stay on the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+struct moe_ctx {
+    moe_config cfg;
+    moe_buffers_desc desc;
+    uint8_t* ws;
+    size_t ws_bytes;
+    int32_t chunks;
+    // Program-order record of the latest moe_layout on this context.
+    bool has_layout;
+    int32_t layout_T;
+    int64_t layout_ntpr4;
+    moe_tuning tuning;
+};
+
+namespace {
+
+constexpr int64_t kAlign = MOE_WORKSPACE_ALIGN;
+
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t elem_bytes(int32_t dtype) {
+    switch (dtype) {
+        case MOE_F32: return 4;
+        case MOE_BF16: return 2;
+        default: return 0;
+    }
+}
+
+int check_config(const moe_config* cfg) {
+    if (!cfg) return MOE_ERR_INVALID_ARG;
+    const int64_t eb = elem_bytes(cfg->dtype);
+    if (eb == 0) return MOE_ERR_INVALID_ARG;
+    if (cfg->num_max_tokens_per_rank < 1) return MOE_ERR_CAPACITY;
+    if (cfg->hidden < 1 || (int64_t(cfg->hidden) * eb) % 16 != 0) return MOE_ERR_INVALID_ARG;
+    if (cfg->num_experts < 1 || cfg->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+    if (cfg->topk < 1 || cfg->topk > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+    const int64_t nmax4 = moe_round_up4(cfg->num_max_tokens_per_rank);
+    // Slot and row indices are int32; keep one spare layout tile of headroom.
+    if (nmax4 * cfg->topk > int64_t(INT32_MAX) - moe::kLayoutTile) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+// Offsets of every buffer; the order puts the small metadata first.
+void plan(const moe_config* cfg, moe_buffers_desc* d) {
+    std::memset(d, 0, sizeof *d);
+    const int64_t E = cfg->num_experts, K = cfg->topk;
+    d->nmax4 = moe_round_up4(cfg->num_max_tokens_per_rank);
+    d->max_rows = d->nmax4 * K;
+    d->row_bytes = int64_t(cfg->hidden) * elem_bytes(cfg->dtype);
+    d->max_tiles = moe::layout_tiles(d->max_rows);
+    d->tile_slots = moe::kLayoutTile;
+    int64_t at = 0;
+    auto take = [&at](int64_t bytes) {
+        const int64_t off = at;
+        at = align_up(at + (bytes > 0 ? bytes : 1));
+        return off;
+    };
+    d->counts = take(E * 4);
+    d->offsets = take((E + 1) * 4);
+    d->block_hist = take(d->max_tiles * E * 4);
+    d->block_base = take(d->max_tiles * E * 4);
+    d->row_map = take(d->max_rows * 4);
+    d->src_map = take(d->max_rows * 4);
+    d->s_e = take(d->max_rows * 4);
+    d->x_e = take(d->max_rows * d->row_bytes);
+    d->y = take(d->nmax4 * d->row_bytes);
+    d->workspace_bytes = at;
+}
+
+template <typename T>
+T* at(const moe_ctx* c, int64_t off) {
+    return reinterpret_cast<T*>(c->ws + off);
+}
+
+// Capacity relation of "API design" for one call; returns the rounded
+// current capacity in *ntpr4.
+int check_call(const moe_ctx* c, int32_t T, int32_t ntpr, int64_t* ntpr4) {
+    if (moe_check_capacity(T, ntpr, c->cfg.num_max_tokens_per_rank) != MOE_OK)
+        return MOE_ERR_CAPACITY;
+    *ntpr4 = moe_round_up4(ntpr);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_ceil_div(int64_t a, int64_t b) {
+    if (a < 0 || b < 1) return -1;
+    return a / b + (a % b != 0 ? 1 : 0);
+}
+
+int64_t moe_round_up4(int64_t n) {
+    if (n < 0) return -1;
+    return (n + 3) & ~int64_t(3);
+}
+
+int64_t moe_num_max_tokens_pretrain(int64_t local_batch, int64_t seq_len, int64_t cp,
+                                    int64_t tp) {
+    if (local_batch < 0 || cp < 1 || tp < 1) return -1;
+    const int64_t per_shard = moe_ceil_div(seq_len, cp * tp);
+    if (per_shard < 0) return -1;
+    return local_batch * per_shard;
+}
+
+int64_t moe_num_max_tokens_infer(int64_t max_num_batched_tokens, int64_t cp, int64_t tp) {
+    if (cp < 1 || tp < 1) return -1;
+    return moe_ceil_div(max_num_batched_tokens, cp * tp);
+}
+
+int moe_validate_num_max(int64_t configured, int64_t derived) {
+    if (configured <= 0 || configured < derived) return MOE_ERR_CAPACITY;
+    return MOE_OK;
+}
+
+int moe_check_capacity(int64_t T, int64_t ntpr, int64_t nmax) {
+    if (nmax < 1 || T < 0 || T > ntpr || ntpr > nmax) return MOE_ERR_CAPACITY;
+    return MOE_OK;
+}
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_CAPACITY:
+            return "capacity relation T <= num_tokens_per_rank <= num_max_tokens_per_rank "
+                   "violated";
+        case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        case MOE_ERR_STATE:
+            return "dispatch/combine does not match the context's latest layout";
+        default: return "unknown status";
+    }
+}
+
+int moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    const int st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    moe_buffers_desc d;
+    plan(cfg, &d);
+    *bytes = static_cast<size_t>(d.workspace_bytes);
+    return MOE_OK;
+}
+
+int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx** out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    const int st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (!d_workspace) return MOE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign != 0) return MOE_ERR_WORKSPACE;
+    moe_buffers_desc d;
+    plan(cfg, &d);
+    if (bytes < static_cast<size_t>(d.workspace_bytes)) return MOE_ERR_WORKSPACE;
+    moe_ctx* c = new (std::nothrow) moe_ctx;
+    if (!c) return MOE_ERR_INVALID_ARG;
+    c->cfg = *cfg;
+    c->desc = d;
+    c->ws = static_cast<uint8_t*>(d_workspace);
+    c->ws_bytes = bytes;
+    c->chunks = static_cast<int32_t>(d.row_bytes / 16);
+    c->has_layout = false;
+    c->layout_T = -1;
+    c->layout_ntpr4 = -1;
+    // Defaults: split long rows so a workgroup's 4 wavefronts share one token's
+    // row; short rows keep one wavefront per token.
+    const int32_t seg = c->chunks >= 512 ? 2 : 1;
+    c->tuning.dispatch_segments = seg;
+    c->tuning.combine_segments = seg;
+    c->tuning.dispatch_nontemporal = 0;
+    *out = c;
+    return MOE_OK;
+}
+
+int moe_destroy(moe_ctx* ctx) {
+    delete ctx;
+    return MOE_OK;
+}
+
+int moe_workspace_offsets(const moe_ctx* ctx, moe_buffers_desc* out) {
+    if (!ctx || !out) return MOE_ERR_INVALID_ARG;
+    *out = ctx->desc;
+    return MOE_OK;
+}
+
+int moe_set_tuning(moe_ctx* ctx, const moe_tuning* t) {
+    if (!ctx || !t) return MOE_ERR_INVALID_ARG;
+    if (t->dispatch_segments < 0 || t->dispatch_segments > moe::kMaxSegments ||
+        t->combine_segments < 0 || t->combine_segments > moe::kMaxSegments)
+        return MOE_ERR_INVALID_ARG;
+    if (t->dispatch_segments) ctx->tuning.dispatch_segments = t->dispatch_segments;
+    if (t->combine_segments) ctx->tuning.combine_segments = t->combine_segments;
+    ctx->tuning.dispatch_nontemporal = t->dispatch_nontemporal ? 1 : 0;
+    return MOE_OK;
+}
+
+int moe_get_tuning(const moe_ctx* ctx, moe_tuning* out) {
+    if (!ctx || !out) return MOE_ERR_INVALID_ARG;
+    *out = ctx->tuning;
+    return MOE_OK;
+}
+
+int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
+               void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    int64_t ntpr4 = 0;
+    const int st = check_call(ctx, T, ntpr, &ntpr4);
+    if (st != MOE_OK) return st;
+    if (T > 0 && !d_topk_ids) return MOE_ERR_INVALID_ARG;
+    const int64_t K = ctx->cfg.topk;
+    moe::LayoutArgs a;
+    a.ids = d_topk_ids;
+    a.nvalid = int64_t(T) * K;
+    a.nslots = ntpr4 * K;
+    a.E = ctx->cfg.num_experts;
+    a.block_hist = at<int32_t>(ctx, ctx->desc.block_hist);
+    a.block_base = at<int32_t>(ctx, ctx->desc.block_base);
+    a.counts = at<int32_t>(ctx, ctx->desc.counts);
+    a.offsets = at<int32_t>(ctx, ctx->desc.offsets);
+    a.row_map = at<int32_t>(ctx, ctx->desc.row_map);
+    a.src_map = at<int32_t>(ctx, ctx->desc.src_map);
+    if (moe::launch_layout(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    ctx->has_layout = true;
+    ctx->layout_T = T;
+    ctx->layout_ntpr4 = ntpr4;
+    return MOE_OK;
+}
+
+int moe_dispatch(moe_ctx* ctx, const void* d_x, const float* d_scores, const int32_t* d_ids,
+                 const int32_t* d_counts, int32_t T, int32_t ntpr, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    int64_t ntpr4 = 0;
+    const int st = check_call(ctx, T, ntpr, &ntpr4);
+    if (st != MOE_OK) return st;
+    if (d_counts != at<int32_t>(ctx, ctx->desc.counts)) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!d_x || !d_scores || !d_ids)) return MOE_ERR_INVALID_ARG;
+    if (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4)
+        return MOE_ERR_STATE;
+    moe::DispatchArgs a;
+    a.x = d_x;
+    a.scores = d_scores;
+    a.row_map = at<int32_t>(ctx, ctx->desc.row_map);
+    a.T = T;
+    a.K = ctx->cfg.topk;
+    a.chunks = ctx->chunks;
+    a.max_rows = ctx->desc.max_rows;
+    a.x_e = at<void>(ctx, ctx->desc.x_e);
+    a.s_e = at<float>(ctx, ctx->desc.s_e);
+    a.segments = ctx->tuning.dispatch_segments;
+    a.nontemporal = ctx->tuning.dispatch_nontemporal != 0;
+    if (moe::launch_dispatch(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
+                const float* d_scores, int32_t T, int32_t ntpr, void* stream, void** d_y_out) {
+    if (!ctx || !d_y_out) return MOE_ERR_INVALID_ARG;
+    int64_t ntpr4 = 0;
+    const int st = check_call(ctx, T, ntpr, &ntpr4);
+    if (st != MOE_OK) return st;
+    if (T > 0 && (!d_y_expert || !d_row_map || !d_scores)) return MOE_ERR_INVALID_ARG;
+    if (d_row_map == at<int32_t>(ctx, ctx->desc.row_map) &&
+        (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4))
+        return MOE_ERR_STATE;
+    moe::CombineArgs a;
+    a.y_e = d_y_expert;
+    a.row_map = d_row_map;
+    a.scores = d_scores;
+    a.T = T;
+    a.K = ctx->cfg.topk;
+    a.chunks = ctx->chunks;
+    a.row_limit = ntpr4 * ctx->cfg.topk;
+    a.bf16 = ctx->cfg.dtype == MOE_BF16;
+    a.y = at<void>(ctx, ctx->desc.y);
+    a.segments = ctx->tuning.combine_segments;
+    if (moe::launch_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    *d_y_out = a.y;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+"""Python binding of the MoE layout / dispatch / combine C ABI.
+
+Argument marshalling only: this module checks tensor placement, dtype and
+shape, passes raw device pointers and torch's current HIP stream to
+libmoe_layout.so, and returns torch views of the library's persistent buffers.
+Every step of the path runs in the library's HIP kernels.
+
+The API follows "Unify expert parallel token dispatcher API" (section "API
+design"): the lifetime maximum num_max_tokens_per_rank sizes the storage once;
+each dispatch takes the current capacity num_tokens_per_rank, with
+x_TD.shape[0] <= num_tokens_per_rank <= num_max_tokens_per_rank. Capacities
+are padded up to a multiple of 4 tokens; padded rows route to no expert and
+combine slices them off ("fix(moe): equalize and align per-rank token counts
+for HybridEP dispatch", section "Fix").
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.float32: L.MOE_F32, torch.bfloat16: L.MOE_BF16}
+
+
+class Layout(NamedTuple):
+    counts: torch.Tensor     # int32 [E], device
+    offsets: torch.Tensor    # int32 [E+1], offsets[E] = total, device
+    row_map: torch.Tensor    # int32 [round_up4(ntpr), K], -1 = no expert
+
+
+class Dispatched(NamedTuple):
+    x_e: torch.Tensor        # [round_up4(ntpr) * K, D] view; rows [0, total) valid
+    s_e: torch.Tensor        # float32 [round_up4(ntpr) * K]; rows [0, total) valid
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def ceil_div(a: int, b: int) -> int:
+    return int(L.load().moe_ceil_div(a, b))
+
+
+def round_up4(n: int) -> int:
+    return int(L.load().moe_round_up4(n))
+
+
+def num_max_tokens_pretrain(local_batch: int, seq_len: int, cp: int = 1, tp: int = 1) -> int:
+    return int(L.load().moe_num_max_tokens_pretrain(local_batch, seq_len, cp, tp))
+
+
+def num_max_tokens_infer(max_num_batched_tokens: int, cp: int = 1, tp: int = 1) -> int:
+    return int(L.load().moe_num_max_tokens_infer(max_num_batched_tokens, cp, tp))
+
+
+def validate_num_max(configured: int, derived: int) -> None:
+    L.check(L.load().moe_validate_num_max(configured, derived), "validate_num_max")
+
+
+class MoeDispatcher:
+    """One persistent workspace for MoE token layout, dispatch and combine.
+
+    The workspace (a uint8 device tensor) is allocated once here, at the
+    lifetime maximum, and carved by the library into fixed-address buffers;
+    no later call allocates, grows, synchronizes or reads back.
+    """
+
+    def __init__(self, num_max_tokens_per_rank: int, hidden: int, num_experts: int,
+                 topk: int, dtype: torch.dtype = torch.bfloat16,
+                 device: Optional[torch.device] = None):
+        if dtype not in _DTYPES:
+            raise TypeError(f"dtype must be one of {list(_DTYPES)}")
+        lib = L.load()
+        self.device = torch.device(device if device is not None else "cuda")
+        if self.device.type != "cuda":
+            raise ValueError("the HIP library needs a GPU device")
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.dtype = dtype
+        self.hidden, self.num_experts, self.topk = hidden, num_experts, topk
+        self.num_max_tokens_per_rank = num_max_tokens_per_rank
+        self._cfg = L.MoeConfig(num_max_tokens_per_rank, hidden, num_experts, topk,
+                                _DTYPES[dtype])
+        nbytes = C.c_size_t(0)
+        L.check(lib.moe_workspace_bytes(C.byref(self._cfg), C.byref(nbytes)),
+                "moe_workspace_bytes")
+        self.workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
+        ctx = C.c_void_p()
+        L.check(lib.moe_create(C.byref(self._cfg), self.workspace.data_ptr(), nbytes.value,
+                               C.byref(ctx)), "moe_create")
+        self._ctx = ctx
+        self._lib = lib
+        d = L.MoeBuffersDesc()
+        L.check(lib.moe_workspace_offsets(ctx, C.byref(d)), "moe_workspace_offsets")
+        self.desc = d
+        E, K, D = num_experts, topk, hidden
+        self.nmax4 = int(d.nmax4)
+        self.counts = self._view(d.counts, E, torch.int32)
+        self.offsets = self._view(d.offsets, E + 1, torch.int32)
+        self.row_map = self._view(d.row_map, d.max_rows, torch.int32).view(self.nmax4, K)
+        self.src_map = self._view(d.src_map, d.max_rows, torch.int32)
+        self.s_e = self._view(d.s_e, d.max_rows, torch.float32)
+        self.x_e = self._view(d.x_e, d.max_rows * D, dtype).view(d.max_rows, D)
+        self.y = self._view(d.y, self.nmax4 * D, dtype).view(self.nmax4, D)
+
+    def _view(self, off: int, n: int, dtype: torch.dtype) -> torch.Tensor:
+        nbytes = int(n) * torch.empty(0, dtype=dtype).element_size()
+        return self.workspace[int(off):int(off) + nbytes].view(dtype)
+
+    def __del__(self):
+        ctx = getattr(self, "_ctx", None)
+        if ctx is not None and ctx.value:
+            self._lib.moe_destroy(ctx)
+            self._ctx = None
+
+    # -- argument checks (marshalling) -------------------------------------
+    def _dev(self, t: torch.Tensor, name: str, dtype: torch.dtype, cols: int) -> torch.Tensor:
+        if t.device != self.device:
+            raise ValueError(f"{name} must be on {self.device}, got {t.device}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.dim() != 2 or t.shape[1] != cols:
+            raise ValueError(f"{name} must be [T, {cols}], got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return t
+
+    def _ntpr(self, T: int, num_tokens_per_rank: Optional[int]) -> int:
+        return T if num_tokens_per_rank is None else int(num_tokens_per_rank)
+
+    # -- the three calls ---------------------------------------------------
+    def layout(self, topk_ids: torch.Tensor, num_tokens_per_rank: Optional[int] = None) -> Layout:
+        """Per-expert counts, offsets and the row map of ids [T, K]."""
+        ids = self._dev(topk_ids, "topk_ids", torch.int32, self.topk)
+        T = ids.shape[0]
+        ntpr = self._ntpr(T, num_tokens_per_rank)
+        L.check(self._lib.moe_layout(self._ctx, ids.data_ptr(), T, ntpr, _stream(self.device)),
+                "moe_layout")
+        n4 = round_up4(ntpr)
+        return Layout(self.counts, self.offsets, self.row_map[:n4])
+
+    def dispatch(self, x_TD: torch.Tensor, topk_scores_TK: torch.Tensor,
+                 topk_expert_ids_TK: torch.Tensor, num_local_tokens_per_expert_E: torch.Tensor,
+                 *, num_tokens_per_rank: Optional[int] = None) -> Dispatched:
+        """Permute x rows and scores into the expert-major buffers using the
+        row map of the preceding layout() on the same ids."""
+        x = self._dev(x_TD, "x_TD", self.dtype, self.hidden)
+        T = x.shape[0]
+        s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
+        ids = self._dev(topk_expert_ids_TK, "topk_expert_ids_TK", torch.int32, self.topk)
+        if s.shape[0] != T or ids.shape[0] != T:
+            raise ValueError("x_TD, topk_scores_TK and topk_expert_ids_TK need the same T")
+        counts = num_local_tokens_per_expert_E
+        ntpr = self._ntpr(T, num_tokens_per_rank)
+        L.check(self._lib.moe_dispatch(self._ctx, x.data_ptr(), s.data_ptr(), ids.data_ptr(),
+                                       counts.data_ptr(), T, ntpr, _stream(self.device)),
+                "moe_dispatch")
+        rows = round_up4(ntpr) * self.topk
+        return Dispatched(self.x_e[:rows], self.s_e[:rows])
+
+    def combine(self, y_expert: torch.Tensor, row_map: torch.Tensor, topk_scores_TK: torch.Tensor,
+                *, num_tokens_per_rank: Optional[int] = None) -> torch.Tensor:
+        """Score-weighted sum of expert outputs back to token order; returns
+        y[:T] (a view of the persistent output buffer)."""
+        s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
+        T = s.shape[0]
+        if y_expert.device != self.device or y_expert.dtype != self.dtype:
+            raise TypeError("y_expert must match the dispatcher's device and dtype")
+        if y_expert.dim() != 2 or y_expert.shape[1] != self.hidden or not y_expert.is_contiguous():
+            raise ValueError(f"y_expert must be a contiguous [rows, {self.hidden}] tensor")
+        rm = row_map
+        if rm.device != self.device or rm.dtype != torch.int32 or not rm.is_contiguous():
+            raise ValueError("row_map must be a contiguous int32 tensor on the device")
+        if rm.dim() != 2 or rm.shape[1] != self.topk or rm.shape[0] < T:
+            raise ValueError(f"row_map must be [>= T, {self.topk}]")
+        ntpr = self._ntpr(T, num_tokens_per_rank)
+        if y_expert.shape[0] < round_up4(ntpr) * self.topk:
+            raise ValueError("y_expert needs round_up4(num_tokens_per_rank) * topk rows")
+        out = C.c_void_p()
+        L.check(self._lib.moe_combine(self._ctx, y_expert.data_ptr(), rm.data_ptr(), s.data_ptr(),
+                                      T, ntpr, _stream(self.device), C.byref(out)),
+                "moe_combine")
+        return self.y[:T]
+
+    # -- tuning ------------------------------------------------------------
+    def set_tuning(self, dispatch_segments: int = 0, combine_segments: int = 0,
+                   dispatch_nontemporal: bool = False) -> None:
+        t = L.MoeTuning(dispatch_segments, combine_segments, int(dispatch_nontemporal))
+        L.check(self._lib.moe_set_tuning(self._ctx, C.byref(t)), "moe_set_tuning")
+
+    def get_tuning(self) -> dict:
+        t = L.MoeTuning()
+        L.check(self._lib.moe_get_tuning(self._ctx, C.byref(t)), "moe_get_tuning")
+        return {"dispatch_segments": t.dispatch_segments, "combine_segments": t.combine_segments,
+                "dispatch_nontemporal": bool(t.dispatch_nontemporal)}

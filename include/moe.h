@@ -1,0 +1,218 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) MoE token layout / dispatch / combine
+ * library (libmoe_layout.so).
+ *
+ * The library does the local, single-GPU work of expert-parallel token
+ * dispatch: it sorts a batch's top-k routing into an expert-major layout,
+ * permutes hidden-state rows and their routing scores into a persistent
+ * expert-major buffer, and gathers expert outputs back into token order as a
+ * score-weighted sum. Sources (web pages, by title and section):
+ *   [TT] "Unify expert parallel token dispatcher API" (torchtitan PR 3970):
+ *        "API design" (dispatch signature; lifetime maximum vs current
+ *        capacity; T <= num_tokens_per_rank <= num_max_tokens_per_rank;
+ *        storage allocated once, never grown, stable addresses for graph
+ *        capture), "Capacity derivation".
+ *   [NA] "fix(moe): equalize and align per-rank token counts for HybridEP
+ *        dispatch" (NeMo Automodel PR 3641): "Problem" (counts must be a
+ *        multiple of 4), "Fix" (padded rows route to no expert with zero
+ *        probability; combine slices the padding off; no extra copies).
+ *   [UC] "ep: graph-safe worst-token HT dispatch+combine" (uccl PR 18):
+ *        "Internode" items 1-3 (no host handshake, per-expert counts on the
+ *        device, the true total from a device-side prefix sum), "Intranode"
+ *        (no host-visible counter shared between calls).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* are HIP device memory on the current device; all
+ *     other pointers are host memory. Element types are fixed: ids int32,
+ *     scores float32, hidden states fp32 or bf16 (config dtype).
+ *   - Matrices are row-major and contiguous: ids and scores [T][K], hidden
+ *     states [T][hidden].
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued on it asynchronously; no call synchronizes,
+ *     allocates device memory, sets memory or copies device-to-host, so the
+ *     moe_layout -> moe_dispatch -> (expert) -> moe_combine sequence can be
+ *     captured into a hipGraph and replayed.
+ *   - Every call returns an int status: MOE_OK (0) or a negative MOE_ERR_*.
+ *     All argument checks run on the host before anything is enqueued; on an
+ *     error nothing was enqueued. MOE_ERR_HIP means a launch failed.
+ *   - Expert ids outside [0, num_experts) (the sentinel -1 included) mean
+ *     "no expert": the slot gets no row and its score is never read.
+ *   - Calls on one context must be ordered on one stream; two streams using
+ *     one context at once race on its buffers.
+ */
+#ifndef MOE_LAYOUT_MOE_H
+#define MOE_LAYOUT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, bad size, unsupported dtype */
+#define MOE_ERR_CAPACITY    (-2) /* capacity relation of [TT] "API design" fails */
+#define MOE_ERR_WORKSPACE   (-3) /* workspace too small or misaligned */
+#define MOE_ERR_HIP         (-4) /* a HIP launch reported an error */
+#define MOE_ERR_STATE       (-5) /* dispatch/combine without a matching layout */
+
+/* Limits checked at create. */
+#define MOE_MAX_EXPERTS   1024
+#define MOE_MAX_TOPK      16
+#define MOE_WORKSPACE_ALIGN 256
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Lifetime configuration ([TT] "API design": the dispatcher configuration
+ * carries num_max_tokens_per_rank).
+ *   num_max_tokens_per_rank  >= 1; buffers hold round_up4 of it tokens
+ *   hidden                   D >= 1, with D * element size a multiple of 16
+ *   num_experts              E, 1..MOE_MAX_EXPERTS
+ *   topk                     K, 1..MOE_MAX_TOPK
+ *   dtype                    moe_dtype of hidden states (x, expert output, y)
+ * round_up4(num_max_tokens_per_rank) * topk must fit in int32. */
+typedef struct moe_config {
+    int32_t num_max_tokens_per_rank;
+    int32_t hidden;
+    int32_t num_experts;
+    int32_t topk;
+    int32_t dtype;
+} moe_config;
+
+/* Byte offsets (into the workspace) and sizes of the persistent buffers,
+ * for callers that view them, e.g. as torch tensors. Every offset is a
+ * multiple of MOE_WORKSPACE_ALIGN.
+ *   counts      int32 [E]            tokens routed to each expert
+ *   offsets     int32 [E+1]          exclusive prefix sum; offsets[E] = total
+ *   row_map     int32 [nmax4][K]     row of slot (t,k) in x_e, -1 = none;
+ *                                    rows [0, round_up4(ntpr)) written by layout
+ *   src_map     int32 [nmax4*K]      t*K+k of the slot at each row; [0,total)
+ *   s_e         f32   [nmax4*K]      score of each dispatched row; [0,total)
+ *   x_e         dtype [nmax4*K][D]   expert-major hidden states; [0,total)
+ *   y           dtype [nmax4][D]     combined output; rows [0,T) of a call
+ *   block_hist, block_base  int32 [max_tiles][E]  layout scratch
+ * nmax4 = round_up4(num_max_tokens_per_rank). */
+typedef struct moe_buffers_desc {
+    int64_t workspace_bytes;
+    int64_t nmax4;
+    int64_t max_rows;      /* nmax4 * K */
+    int64_t row_bytes;     /* D * element size */
+    int64_t max_tiles;     /* layout tiles at full capacity */
+    int64_t tile_slots;    /* (t,k) slots per layout tile */
+    int64_t counts, offsets, row_map, src_map, s_e, x_e, y;
+    int64_t block_hist, block_base;
+} moe_buffers_desc;
+
+/* Opaque per-workspace context; host memory only. */
+typedef struct moe_ctx moe_ctx;
+
+/* Bytes of device workspace a context with this configuration needs.
+ * Pure host. MOE_ERR_INVALID_ARG for an invalid configuration. */
+int moe_workspace_bytes(const moe_config *cfg, size_t *bytes);
+
+/* Create a context over a caller-owned device workspace of `bytes` bytes
+ * (>= moe_workspace_bytes, aligned to MOE_WORKSPACE_ALIGN). The buffers are
+ * carved from it once, at fixed addresses; no call ever allocates or grows
+ * them ([TT] "API design"). The caller keeps the workspace alive until
+ * moe_destroy and frees it afterwards. Pure host; *out receives the context. */
+int moe_create(const moe_config *cfg, void *d_workspace, size_t bytes, moe_ctx **out);
+
+/* Free the host-side context (not the workspace). NULL is accepted. */
+int moe_destroy(moe_ctx *ctx);
+
+/* Fill *out with the buffer offsets and sizes of this context. Pure host. */
+int moe_workspace_offsets(const moe_ctx *ctx, moe_buffers_desc *out);
+
+/* Routing layout ([TT] "API design": per-expert token counts; [UC]
+ * "Internode" 2 and 3). From d_topk_ids [T][K] computes into the context:
+ *   counts[e], offsets[0..E] (offsets[E] = total valid slots, on the device),
+ *   row_map[t][k] for t < round_up4(num_tokens_per_rank): the row of slot
+ *     (t,k) in the expert-major buffer, rows of one expert ordered by
+ *     ascending t*K+k; -1 for no expert and for padding rows t >= T,
+ *   src_map[row] = t*K+k for rows [0,total).
+ * Requires 0 <= T <= num_tokens_per_rank <= num_max_tokens_per_rank
+ * (MOE_ERR_CAPACITY otherwise). Only ids rows [0,T) are read; d_topk_ids may
+ * be NULL when T == 0. Records (T, round_up4(num_tokens_per_rank)) on the
+ * host as the context's current layout. */
+int moe_layout(moe_ctx *ctx, const int32_t *d_topk_ids, int32_t T,
+               int32_t num_tokens_per_rank, void *stream);
+
+/* Dispatch ([TT] "API design" signature; [NA] "Fix"). Permutes the hidden
+ * states into the context's expert-major buffer using the row map of the
+ * preceding moe_layout on this context:
+ *   x_e[row_map[t][k]] = x[t] (bit copy), s_e[row_map[t][k]] = scores[t][k]
+ * for t < T and every slot with an expert. Padding rows [T,
+ * round_up4(num_tokens_per_rank)) are never copied.
+ *   d_x         [T][D] hidden states (config dtype)
+ *   d_topk_scores [T][K] float32; d_topk_ids [T][K] int32 (the ids the
+ *               layout was built from; the kernels use the row map instead)
+ *   d_counts    must be the context's own counts buffer (as written by
+ *               moe_layout); any other pointer is MOE_ERR_INVALID_ARG
+ * T and num_tokens_per_rank must equal those of the most recent moe_layout
+ * call on this context (MOE_ERR_STATE otherwise). Rows [0, offsets[E]) of x_e
+ * and s_e are written; the rest is left as it was. */
+int moe_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
+                 const int32_t *d_topk_ids, const int32_t *d_counts, int32_t T,
+                 int32_t num_tokens_per_rank, void *stream);
+
+/* Combine ([NA] "Fix" and "Testing"). For t < T:
+ *   y[t] = sum over k = 0..K-1 with d_row_map[t][k] >= 0 of
+ *          scores[t][k] * y_expert[d_row_map[t][k]]
+ * accumulated in fp32 with fused multiply-add in ascending k from +0.0 and
+ * stored in the config dtype (bf16 rounds to nearest even; NaN -> 0x7FC0).
+ * A slot with row -1 is skipped and its score is never read; a token with no
+ * expert gets +0.0. Rows >= T (the padding) are not computed.
+ *   d_y_expert  expert outputs in the expert-major layout,
+ *               [>= round_up4(num_tokens_per_rank) * K][D] (the worst-case
+ *               total, known on the host; only rows [0,total) are read).
+ *               The context's x_e serves for an identity expert.
+ *   d_row_map   [>= T][K] row map, normally the context's; when it is the
+ *               context's, T and num_tokens_per_rank must match the most
+ *               recent moe_layout (MOE_ERR_STATE otherwise)
+ *   d_topk_scores [T][K] float32
+ *   *d_y_out    receives the device address of y ([nmax4][D], rows [0,T)
+ *               valid until the next combine on this context).
+ * Rows of d_row_map outside [0, round_up4(num_tokens_per_rank) * K) are
+ * treated as no expert. */
+int moe_combine(moe_ctx *ctx, const void *d_y_expert, const int32_t *d_row_map,
+                const float *d_topk_scores, int32_t T, int32_t num_tokens_per_rank,
+                void *stream, void **d_y_out);
+
+/* Launch shape tuning (optional). Each token row is split into `segments`
+ * wavefront work items (1..16); 0 keeps the current value. nontemporal != 0
+ * marks dispatch's expert-buffer stores as streaming. Pure host. */
+typedef struct moe_tuning {
+    int32_t dispatch_segments;
+    int32_t combine_segments;
+    int32_t dispatch_nontemporal;
+} moe_tuning;
+int moe_set_tuning(moe_ctx *ctx, const moe_tuning *tuning);
+int moe_get_tuning(const moe_ctx *ctx, moe_tuning *out);
+
+/* Capacity helpers ([TT] "Capacity derivation"; [NA] "Fix"). Pure host.
+ * Invalid arguments (negative sizes, degrees < 1) return -1. */
+int64_t moe_ceil_div(int64_t a, int64_t b);                 /* a >= 0, b >= 1 */
+int64_t moe_round_up4(int64_t n);                           /* n >= 0 */
+/* local_batch_size * ceil_div(seq_len, cp * tp) */
+int64_t moe_num_max_tokens_pretrain(int64_t local_batch, int64_t seq_len,
+                                    int64_t cp, int64_t tp);
+/* ceil_div(max_num_batched_tokens, cp * tp) */
+int64_t moe_num_max_tokens_infer(int64_t max_num_batched_tokens, int64_t cp,
+                                 int64_t tp);
+/* An explicitly configured maximum must be positive and >= the derived
+ * requirement: MOE_OK, or MOE_ERR_CAPACITY. */
+int moe_validate_num_max(int64_t configured, int64_t derived);
+/* The capacity relation 0 <= T <= ntpr <= nmax, nmax >= 1: MOE_OK or
+ * MOE_ERR_CAPACITY. */
+int moe_check_capacity(int64_t T, int64_t num_tokens_per_rank,
+                       int64_t num_max_tokens_per_rank);
+
+/* Static description of a status code. */
+const char *moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYOUT_MOE_H */

@@ -10,3 +10,18 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a visible GPU; without one (a CPU-only host) they are
+    skipped. With a GPU present, a missing HIP library fails them loudly."""
+    if not any("gpu" in item.keywords for item in items):
+        return
+    import pytest
+    import torch
+    if torch.cuda.is_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

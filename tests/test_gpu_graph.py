@@ -1,0 +1,129 @@
+"""hipGraph capture and replay of layout -> dispatch -> expert -> combine.
+
+Worst-token mode ("ep: graph-safe worst-token HT dispatch+combine", sections
+"Summary" and "Tests"): the graph is captured once at the lifetime maximum
+(8192 tokens); before each replay fresh routing is written into the captured
+input tensors with rows past the replay's T set to id -1 and score 0. Every
+replay is checked against the oracle on its own T, some against an eager run
+of the same inputs bitwise, and eager calls on the same context are
+interleaved with the replays."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from combine_moe_layout_05_amd import MoeDispatcher
+
+from gpu_util import (DEV, ORACLE_THREADS, assert_combine_within_bar, f32_dev, i32_dev,
+                      note, x_to_dev, x_to_np)
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS["graph"]
+CHUNKS = 4
+PER_CHUNK = workloads.GRAPH_REPLAYS // CHUNKS
+
+
+def _double_bf16(x_bits: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16) * 2
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+class Captured:
+    """Static inputs, the dispatcher and one captured graph."""
+
+    def __init__(self):
+        N, D, K = W.nmax, W.D, W.K
+        self.disp = MoeDispatcher(N, D, W.E, K, dtype=torch.bfloat16, device=DEV)
+        self.x = torch.zeros((N, D), dtype=torch.bfloat16, device=DEV)
+        self.ids = torch.full((N, K), -1, dtype=torch.int32, device=DEV)
+        self.s = torch.zeros((N, K), dtype=torch.float32, device=DEV)
+        self.y_e = torch.zeros((self.disp.desc.max_rows, D), dtype=torch.bfloat16, device=DEV)
+        side = torch.cuda.Stream(device=DEV)
+        side.wait_stream(torch.cuda.current_stream(DEV))
+        with torch.cuda.stream(side):          # warm-up outside the capture
+            self._body()
+        torch.cuda.current_stream(DEV).wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.y = self._body()
+        torch.cuda.synchronize()
+        self.eager_calls = 0
+
+    def _body(self):
+        d = self.disp
+        lay = d.layout(self.ids, W.nmax)
+        d.dispatch(self.x, self.s, self.ids, lay.counts, num_tokens_per_rank=W.nmax)
+        torch.mul(d.x_e, 2, out=self.y_e)      # the expert: exact doubling in bf16
+        return d.combine(self.y_e, lay.row_map, self.s, num_tokens_per_rank=W.nmax)
+
+    def load(self, b):
+        T = b["T"]
+        self.x[:T].copy_(x_to_dev(b["x"]))
+        self.x[T:].zero_()
+        self.ids[:T].copy_(i32_dev(b["ids"]))
+        self.ids[T:].fill_(-1)
+        self.s[:T].copy_(f32_dev(b["scores"]))
+        self.s[T:].zero_()
+
+    def eager(self, x, ids, scores, T, ntpr):
+        d = self.disp
+        ids_d, s_d = i32_dev(ids[:T]), f32_dev(scores[:T])
+        lay = d.layout(ids_d, ntpr)
+        d.dispatch(x_to_dev(x[:T]), s_d, ids_d, lay.counts, num_tokens_per_rank=ntpr)
+        ye = d.x_e[: lay.row_map.shape[0] * W.K] * 2
+        y = d.combine(ye, lay.row_map, s_d, num_tokens_per_rank=ntpr)
+        torch.cuda.synchronize()
+        self.eager_calls += 1
+        return x_to_np(y), lay.counts.cpu().numpy(), lay.offsets.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def cap():
+    note("graph: capture at 8192 tokens")
+    c = Captured()
+    yield c
+    del c
+    torch.cuda.empty_cache()
+
+
+def _oracle(b, T, ntpr):
+    return oracle.run_pipeline(_double_bf16(b["x"][:T]), b["ids"], b["scores"], T, ntpr,
+                               W.E, W.K, nthreads=ORACLE_THREADS)
+
+
+@pytest.mark.parametrize("chunk", range(CHUNKS))
+def test_graph_replays_with_fresh_routing(cap, chunk):
+    for i in range(chunk * PER_CHUNK, (chunk + 1) * PER_CHUNK):
+        b = workloads.replay_batch(i)
+        T = b["T"]
+        note(f"graph replay {i} T={T}")
+        cap.load(b)
+        cap.graph.replay()
+        torch.cuda.synchronize()
+        y = x_to_np(cap.y)
+        o = _oracle(b, T, T)
+        np.testing.assert_array_equal(cap.disp.counts.cpu().numpy(), o["counts"])
+        assert int(cap.disp.offsets[-1].item()) == o["total"] == T * W.K
+        assert_combine_within_bar(y[:T], o["y"])
+        assert np.array_equal(y[:T], o["y"])
+        assert (y[T:] == 0).all()               # sentinel rows: +0.0, sliced off
+        if i % 10 == 5:
+            # replay == eager run of the same inputs, bitwise
+            ye, ce, _ = cap.eager(b["x"], b["ids"], b["scores"], T, T)
+            assert np.array_equal(ye, y[:T])
+            np.testing.assert_array_equal(ce, o["counts"])
+        if i % 10 == 9:
+            # an unrelated eager batch on the same context between replays
+            w2 = workloads.Workload("interleave", T=777 + i, ntpr=800 + i, nmax=W.nmax, D=W.D,
+                                    E=W.E, K=W.K, dtype="bf16", routing="zipf", zipf_s=1.1,
+                                    seed=5000 + i)
+            b2 = workloads.make_batch(w2)
+            note(f"eager interleave after replay {i}: T={w2.T} ntpr={w2.ntpr}")
+            ye, ce, oe = cap.eager(b2["x"], b2["ids"], b2["scores"], w2.T, w2.ntpr)
+            o2 = _oracle(b2, w2.T, w2.ntpr)
+            np.testing.assert_array_equal(ce, o2["counts"])
+            np.testing.assert_array_equal(oe, o2["offsets"])
+            assert np.array_equal(ye, o2["y"])

@@ -1,0 +1,189 @@
+"""CPU tests of the C-ABI library's host side: it loads, exports every entry
+point include/moe.h declares, and its pure-host logic (capacity helpers,
+configuration checks, workspace carve-up, argument validation) behaves as the
+pages state. No call here launches a kernel."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from combine_moe_layout_05_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert "moe_layout" in names and "moe_dispatch" in names and "moe_combine" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def test_capacity_helpers_agree_with_oracle(lib):
+    rng = np.random.default_rng(0)
+    for a, b in zip(rng.integers(-3, 10**7, 300), rng.integers(-1, 5000, 300)):
+        assert lib.moe_ceil_div(int(a), int(b)) == oracle.ceil_div(int(a), int(b))
+    for n in range(-3, 3000):
+        assert lib.moe_round_up4(n) == oracle.round_up4(n)
+    cases = [(8, 4096, 1, 1), (8, 4097, 2, 4), (1, 32768, 1, 1), (3, 100, 3, 3),
+             (0, 5, 1, 1), (2, 5, 0, 1), (-1, 5, 1, 1)]
+    for c in cases:
+        assert lib.moe_num_max_tokens_pretrain(*c) == oracle.num_max_pretrain(*c)
+    for c in [(8192, 2, 2), (8193, 2, 2), (1, 8, 1), (10, 0, 1)]:
+        assert lib.moe_num_max_tokens_infer(*c) == oracle.num_max_infer(*c)
+    for conf, der in [(0, 1), (-4, -8), (4103, 4104), (4104, 4104), (8192, 4104)]:
+        assert (lib.moe_validate_num_max(conf, der) == 0) == (oracle.validate_num_max(conf, der) == 0)
+    for T in range(-1, 12):
+        for ntpr in range(-1, 12):
+            for nmax in range(-1, 12):
+                assert (lib.moe_check_capacity(T, ntpr, nmax) == 0) == \
+                       (oracle.check_capacity(T, ntpr, nmax) == 0)
+
+
+def _cfg(nmax=4096, D=7168, E=256, K=8, dtype=L.MOE_BF16):
+    return L.MoeConfig(nmax, D, E, K, dtype)
+
+
+def _bytes(lib, cfg):
+    n = C.c_size_t(0)
+    st = lib.moe_workspace_bytes(C.byref(cfg), C.byref(n))
+    return st, n.value
+
+
+def test_config_validation(lib):
+    assert _bytes(lib, _cfg())[0] == L.MOE_OK
+    assert _bytes(lib, _cfg(nmax=0))[0] == L.MOE_ERR_CAPACITY
+    assert _bytes(lib, _cfg(D=7))[0] == L.MOE_ERR_INVALID_ARG       # 14 B rows
+    assert _bytes(lib, _cfg(D=4, dtype=L.MOE_F32))[0] == L.MOE_OK   # 16 B rows
+    assert _bytes(lib, _cfg(D=4))[0] == L.MOE_ERR_INVALID_ARG       # 8 B bf16 rows
+    assert _bytes(lib, _cfg(E=0))[0] == L.MOE_ERR_INVALID_ARG
+    assert _bytes(lib, _cfg(E=L.MOE_MAX_EXPERTS + 1))[0] == L.MOE_ERR_INVALID_ARG
+    assert _bytes(lib, _cfg(K=0))[0] == L.MOE_ERR_INVALID_ARG
+    assert _bytes(lib, _cfg(K=L.MOE_MAX_TOPK + 1))[0] == L.MOE_ERR_INVALID_ARG
+    assert _bytes(lib, _cfg(dtype=7))[0] == L.MOE_ERR_INVALID_ARG
+    assert _bytes(lib, _cfg(nmax=2**31 - 1, K=16))[0] == L.MOE_ERR_INVALID_ARG  # int32 rows
+    assert lib.moe_workspace_bytes(None, None) == L.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("nmax,D,E,K,dtype", [
+    (4096, 7168, 256, 8, L.MOE_BF16), (64, 128, 8, 2, L.MOE_F32),
+    (4097, 2048, 128, 8, L.MOE_BF16), (32768, 7168, 256, 8, L.MOE_BF16),
+    (1, 8, 1, 1, L.MOE_BF16), (8192, 4096, 1024, 16, L.MOE_BF16)])
+def test_workspace_carve_up(lib, nmax, D, E, K, dtype):
+    cfg = _cfg(nmax, D, E, K, dtype)
+    st, nbytes = _bytes(lib, cfg)
+    assert st == L.MOE_OK
+    fake = 1 << 40                                   # never dereferenced on the host
+    ctx = C.c_void_p()
+    assert lib.moe_create(C.byref(cfg), fake, nbytes, C.byref(ctx)) == L.MOE_OK
+    d = L.MoeBuffersDesc()
+    assert lib.moe_workspace_offsets(ctx, C.byref(d)) == L.MOE_OK
+    eb = 4 if dtype == L.MOE_F32 else 2
+    n4 = oracle.round_up4(nmax)
+    assert d.nmax4 == n4 and d.max_rows == n4 * K and d.row_bytes == D * eb
+    sizes = {"counts": E * 4, "offsets": (E + 1) * 4, "row_map": n4 * K * 4,
+             "src_map": n4 * K * 4, "s_e": n4 * K * 4, "x_e": n4 * K * D * eb,
+             "y": n4 * D * eb, "block_hist": d.max_tiles * E * 4,
+             "block_base": d.max_tiles * E * 4}
+    assert d.max_tiles * d.tile_slots >= n4 * K
+    spans = sorted((getattr(d, k), getattr(d, k) + v, k) for k, v in sizes.items())
+    for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (ka, kb)                    # no overlap
+    for off, _, k in spans:
+        assert off % L.MOE_WORKSPACE_ALIGN == 0, k
+    assert spans[-1][1] <= d.workspace_bytes == nbytes
+    assert lib.moe_destroy(ctx) == L.MOE_OK
+
+
+def _ctx(lib, cfg):
+    st, nbytes = _bytes(lib, cfg)
+    ctx = C.c_void_p()
+    assert lib.moe_create(C.byref(cfg), 1 << 40, nbytes, C.byref(ctx)) == L.MOE_OK
+    d = L.MoeBuffersDesc()
+    lib.moe_workspace_offsets(ctx, C.byref(d))
+    return ctx, d, nbytes
+
+
+def test_create_rejects_bad_workspace(lib):
+    cfg = _cfg(64, 128, 8, 2, L.MOE_F32)
+    st, nbytes = _bytes(lib, cfg)
+    ctx = C.c_void_p()
+    assert lib.moe_create(C.byref(cfg), 1 << 40, nbytes - 1, C.byref(ctx)) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_create(C.byref(cfg), (1 << 40) + 16, nbytes, C.byref(ctx)) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_create(C.byref(cfg), None, nbytes, C.byref(ctx)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_create(C.byref(cfg), 1 << 40, nbytes, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_destroy(None) == L.MOE_OK
+
+
+def test_calls_reject_bad_arguments_before_enqueueing(lib):
+    # Every case below fails a host check, so no kernel is launched.
+    cfg = _cfg(4096, 2048, 128, 8, L.MOE_BF16)
+    ctx, d, _ = _ctx(lib, cfg)
+    base = 1 << 40
+    counts = base + d.counts
+    row_map = base + d.row_map
+    ids = x = s = 1 << 41
+    out = C.c_void_p()
+    # capacity relation T <= ntpr <= nmax
+    assert lib.moe_layout(ctx, ids, 2049, 2048, None) == L.MOE_ERR_CAPACITY
+    assert lib.moe_layout(ctx, ids, 10, 4097, None) == L.MOE_ERR_CAPACITY
+    assert lib.moe_layout(ctx, ids, -1, 8, None) == L.MOE_ERR_CAPACITY
+    assert lib.moe_layout(ctx, None, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_layout(None, ids, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    # dispatch / combine before any layout on this context
+    assert lib.moe_dispatch(ctx, x, s, ids, counts, 5, 8, None) == L.MOE_ERR_STATE
+    assert lib.moe_combine(ctx, base + d.x_e, row_map, s, 5, 8, None, C.byref(out)) == L.MOE_ERR_STATE
+    # counts must be the context's own buffer
+    assert lib.moe_dispatch(ctx, x, s, ids, counts + 256, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctx, None, s, ids, counts, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctx, x, s, ids, counts, 4097, 4097, None) == L.MOE_ERR_CAPACITY
+    assert lib.moe_combine(ctx, None, row_map, s, 5, 8, None, C.byref(out)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctx, base + d.x_e, row_map, s, 5, 8, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctx, base + d.x_e, row_map, s, 9, 8, None, C.byref(out)) == L.MOE_ERR_CAPACITY
+    lib.moe_destroy(ctx)
+
+
+def test_tuning_roundtrip_and_limits(lib):
+    ctx, _, _ = _ctx(lib, _cfg())
+    t = L.MoeTuning()
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
+    assert 1 <= t.dispatch_segments <= 16 and 1 <= t.combine_segments <= 16
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1))) == L.MOE_OK
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
+    assert (t.dispatch_segments, t.combine_segments, t.dispatch_nontemporal) == (4, 3, 1)
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(17, 1, 0))) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(-1, 1, 0))) == L.MOE_ERR_INVALID_ARG
+    lib.moe_destroy(ctx)
+
+
+def test_strerror_covers_every_status(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        msg = lib.moe_strerror(st).decode()
+        assert msg and msg != "unknown status"
+    assert lib.moe_strerror(-99).decode() == "unknown status"
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "combine_moe_layout_05_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "moe_oracle" not in text and "liborc" not in text, f
