@@ -49,10 +49,13 @@ def parse_args():
                    help="budget of the oracle CPU baseline (0 = skip)")
     p.add_argument("--dispatch-segments", type=int, default=0)
     p.add_argument("--combine-segments", type=int, default=0)
-    p.add_argument("--nontemporal", type=int, default=-1,
+    p.add_argument("--dispatch-nontemporal", type=int, default=-1,
                    help="1/0 forces dispatch's streaming stores on/off; -1 keeps the default")
+    p.add_argument("--combine-nontemporal", type=int, default=-1,
+                   help="1/0 forces combine's streaming loads on/off; -1 keeps the default")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
-                   help="only run a plain device copy of this size (for counter scaling)")
+                   help="only run plain device write/read/copy of this size (HBM ceiling, "
+                        "counter scaling)")
     return p.parse_args()
 
 
@@ -92,17 +95,33 @@ def counter_traffic(kind: str, workload: str):
 
 
 def calibrate_copy(mib: int) -> None:
+    """Plain device write, read and copy of `mib` MiB through torch's own
+    kernels: the rates a streaming kernel can reach on this GPU, and (under
+    rocprofv3 counters) the bytes the counters report for a known size."""
     import torch
     n = mib << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
+    b.fill_(2)
     torch.cuda.synchronize()
-    for _ in range(5):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n,
-                      "bytes_written_per_launch": n, "launches": 5}), flush=True)
+    res = {"calibration": "device write/read/copy", "bytes": n}
+    ops = {"write": (lambda: a.fill_(3), n),
+           "read": (lambda: a.view(torch.float32).sum(), n),
+           "copy": (lambda: b.copy_(a), 2 * n)}
+    for name, (fn, nbytes) in ops.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name] = {"us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    print(json.dumps(res), flush=True)
 
 
 def main() -> int:
@@ -138,11 +157,12 @@ def main() -> int:
     ids = torch.from_numpy(b["ids"]).to(dev)
     s = torch.from_numpy(b["scores"]).to(dev)
     disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=dev)
-    if args.dispatch_segments or args.combine_segments or args.nontemporal >= 0:
-        cur = disp.get_tuning()
-        disp.set_tuning(args.dispatch_segments, args.combine_segments,
-                        bool(args.nontemporal) if args.nontemporal >= 0
-                        else cur["dispatch_nontemporal"])
+    cur = disp.get_tuning()
+    disp.set_tuning(args.dispatch_segments, args.combine_segments,
+                    bool(args.dispatch_nontemporal) if args.dispatch_nontemporal >= 0
+                    else cur["dispatch_nontemporal"],
+                    bool(args.combine_nontemporal) if args.combine_nontemporal >= 0
+                    else cur["combine_nontemporal"])
     tuning = disp.get_tuning()
     ntpr = w.ntpr
 

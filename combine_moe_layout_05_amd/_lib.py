@@ -40,12 +40,12 @@ class MoeBuffersDesc(C.Structure):
     _fields_ = [(n, _i64) for n in (
         "workspace_bytes", "nmax4", "max_rows", "row_bytes", "max_tiles", "tile_slots",
         "counts", "offsets", "row_map", "src_map", "s_e", "x_e", "y",
-        "block_hist", "block_base")]
+        "block_hist")]
 
 
 class MoeTuning(C.Structure):
     _fields_ = [("dispatch_segments", _i32), ("combine_segments", _i32),
-                ("dispatch_nontemporal", _i32)]
+                ("dispatch_nontemporal", _i32), ("combine_nontemporal", _i32)]
 
 
 SIGNATURES = {

@@ -12,10 +12,13 @@
 // computed; padding rows are never materialized.
 //
 // Bound by HBM reads (K rows read per row written). One wavefront per
-// (token, row segment); per 16-byte chunk each lane issues the K row loads
-// back to back before any arithmetic, so K x U loads are in flight per lane.
-// No-expert slots load the token's first valid row instead (always written,
-// finite) and discard it, which keeps every load unconditional.
+// (token, row segment); each lane owns one 16-byte chunk per iteration and
+// issues its K row loads back to back. When every slot of the token has an
+// expert (the common case) the loop is double-buffered: the next chunk's K
+// loads are issued before the current chunk is reduced and stored, and no
+// per-slot branch sits between loads and their use. Otherwise no-expert slots
+// load the token's first valid row instead (always written, finite) and skip
+// it in the sum, which keeps every load unconditional.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -73,7 +76,15 @@ struct Lanes<true> {  // 8 bf16 per 16-byte chunk, element 2i in the low half
     }
 };
 
-template <int K, bool BF16, int U>
+template <bool NT>
+__device__ __forceinline__ v4i fetch(const v4i* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <int K, bool BF16, bool NT>
 __global__ __launch_bounds__(kMoveThreads)
 void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row_map,
                     const float* __restrict__ scores, int32_t T, int32_t chunks,
@@ -108,15 +119,18 @@ void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row
     int32_t row[K];
     float s[K];
     int32_t fallback = -1;
+    bool all_valid = true;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         row[k] = __builtin_amdgcn_readfirstlane(tile_rows[lt * K + k]);
         s[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tile_scores[lt * K + k])));
         if (fallback < 0 && row[k] >= 0) fallback = row[k];
+        all_valid = all_valid && row[k] >= 0;
     }
 
     const int32_t c_begin = seg * seg_chunks;
     const int32_t c_end = min(c_begin + seg_chunks, chunks);
+    const int32_t iters = (c_end - c_begin + 63) / 64;   // one chunk per lane each
     v4i* dst = y + t * chunks;
 
     if (fallback < 0) {  // no slot reaches an expert: +0.0
@@ -129,38 +143,65 @@ void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row
 #pragma unroll
     for (int k = 0; k < K; ++k) src[k] = y_e + int64_t(row[k] >= 0 ? row[k] : fallback) * chunks;
 
-    for (int32_t c0 = c_begin; c0 < c_end; c0 += 64 * U) {
-        v4i v[U][K];
+    // Chunk of iteration i for this lane; the last iteration's lanes past
+    // the segment end re-load its last chunk and do not store.
+    auto chunk_of = [&](int32_t i) { return min(c_begin + i * 64 + lane, c_end - 1); };
+    auto load = [&](v4i (&b)[K], int32_t i) {
+        const int32_t c = chunk_of(i);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t c = min(c0 + u * 64 + lane, c_end - 1);
-#pragma unroll
-            for (int k = 0; k < K; ++k) v[u][k] = src[k][c];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int k = 0; k < K; ++k) b[k] = fetch<NT>(src[k] + c);
+    };
+
+    if (all_valid) {
+        // Every slot has an expert: no per-slot test, loads of the next chunk
+        // are in flight while this one is reduced and stored.
+        auto emit = [&](const v4i (&b)[K], int32_t i) {
             float acc[L::N];
 #pragma unroll
-            for (int i = 0; i < L::N; ++i) acc[i] = 0.0f;
+            for (int e = 0; e < L::N; ++e) acc[e] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                if (row[k] >= 0) L::fma_into(acc, s[k], v[u][k]);
-            const int32_t c = c0 + u * 64 + lane;
+            for (int k = 0; k < K; ++k) L::fma_into(acc, s[k], b[k]);
+            const int32_t c = c_begin + i * 64 + lane;
             if (c < c_end) dst[c] = L::pack(acc);
+        };
+        v4i b0[K], b1[K];
+        load(b0, 0);
+        int32_t i = 0;
+        for (; i + 1 < iters; i += 2) {
+            load(b1, i + 1);
+            emit(b0, i);
+            load(b0, min(i + 2, iters - 1));
+            emit(b1, i + 1);
         }
+        if (i < iters) emit(b0, i);
+        return;
+    }
+
+    // Some slots without an expert: they are skipped (their loaded data and
+    // score never enter the sum).
+    for (int32_t i = 0; i < iters; ++i) {
+        v4i b[K];
+        load(b, i);
+        float acc[L::N];
+#pragma unroll
+        for (int e = 0; e < L::N; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (row[k] >= 0) L::fma_into(acc, s[k], b[k]);
+        const int32_t c = c_begin + i * 64 + lane;
+        if (c < c_end) dst[c] = L::pack(acc);
     }
 }
 
 template <int K, bool BF16>
 hipError_t launch_k(const CombineArgs& a, int32_t segments, int32_t seg_chunks,
                     hipStream_t stream) {
-    constexpr int U = K <= 4 ? 4 : 2;
     const int64_t items = int64_t(a.T) * segments;
     const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    hipLaunchKernelGGL((combine_kernel<K, BF16, U>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kMoveThreads), 0, stream, static_cast<const v4i*>(a.y_e),
-                       a.row_map, a.scores, a.T, a.chunks, segments, seg_chunks, a.row_limit,
-                       static_cast<v4i*>(a.y));
+    auto kernel = a.nontemporal ? combine_kernel<K, BF16, true> : combine_kernel<K, BF16, false>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kMoveThreads), 0, stream,
+                       static_cast<const v4i*>(a.y_e), a.row_map, a.scores, a.T, a.chunks,
+                       segments, seg_chunks, a.row_limit, static_cast<v4i*>(a.y));
     return hipGetLastError();
 }
 

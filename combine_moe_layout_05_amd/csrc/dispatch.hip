@@ -15,8 +15,9 @@
 // read). One wavefront takes one (token, row segment) item: it loads the
 // segment once, 16 bytes per lane so each wavefront access is a contiguous
 // 1 KiB run, and stores it K times. The workgroup's row-map entries (at most
-// 4 tokens x K) are staged in LDS with one coalesced load and read back as
-// wavefront-uniform scalars, so the destination addresses live in SGPRs.
+// 4 tokens x K) are staged in LDS with one coalesced load and moved into
+// SGPRs once per wavefront, so the K destination row addresses are scalar
+// and the per-slot "has an expert" test is a scalar branch.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -24,13 +25,24 @@ namespace {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
-template <int U, bool NT>
+constexpr int kDispatchUnroll = 4;   // 16-byte chunks per lane in flight
+
+template <bool NT>
+__device__ __forceinline__ void put(v4i* p, v4i v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+template <int K, bool NT>
 __global__ __launch_bounds__(kMoveThreads)
 void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores,
-                     const int32_t* __restrict__ row_map, int32_t T, int32_t K,
-                     int32_t chunks, int32_t segments, int32_t seg_chunks,
-                     int64_t max_rows, v4i* __restrict__ x_e, float* __restrict__ s_e) {
-    __shared__ int32_t tile_rows[kMoveWaves * kMaxTopk];
+                     const int32_t* __restrict__ row_map, int32_t T, int32_t chunks,
+                     int32_t segments, int32_t seg_chunks, int64_t max_rows,
+                     v4i* __restrict__ x_e, float* __restrict__ s_e) {
+    constexpr int U = kDispatchUnroll;
+    __shared__ int32_t tile_rows[kMoveWaves * K];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -50,50 +62,55 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     const int64_t t = item / segments;
     if (t >= T) return;
     const int seg = static_cast<int>(item - t * segments);
-    const int32_t* rows = tile_rows + (t - t_first) * K;
+    const int lt = static_cast<int>(t - t_first);
+
+    int32_t row[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) row[k] = __builtin_amdgcn_readfirstlane(tile_rows[lt * K + k]);
 
     if (seg == 0 && lane < K) {
-        const int32_t r = rows[lane];
+        const int32_t r = tile_rows[lt * K + lane];
         if (r >= 0) s_e[r] = scores[t * K + lane];
     }
 
     const int32_t c_begin = seg * seg_chunks;
     const int32_t c_end = min(c_begin + seg_chunks, chunks);
     const v4i* src = x + t * chunks;
-    for (int32_t c0 = c_begin; c0 < c_end; c0 += 64 * U) {
+    int32_t c0 = c_begin;
+    // Whole groups: every lane has U chunks in range.
+    for (; c0 + 64 * U <= c_end; c0 += 64 * U) {
         v4i v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t c = c0 + u * 64 + lane;
-            if (c < c_end) v[u] = src[c];
-        }
-        for (int k = 0; k < K; ++k) {
-            const int32_t r = __builtin_amdgcn_readfirstlane(rows[k]);
-            if (r < 0) continue;
-            v4i* dst = x_e + int64_t(r) * chunks;
+        for (int u = 0; u < U; ++u) v[u] = src[c0 + u * 64 + lane];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t c = c0 + u * 64 + lane;
-                if (c < c_end) {
-                    if constexpr (NT)
-                        __builtin_nontemporal_store(v[u], dst + c);
-                    else
-                        dst[c] = v[u];
-                }
-            }
+        for (int k = 0; k < K; ++k) {
+            if (row[k] < 0) continue;
+            v4i* dst = x_e + int64_t(row[k]) * chunks + c0 + lane;
+#pragma unroll
+            for (int u = 0; u < U; ++u) put<NT>(dst + u * 64, v[u]);
         }
+    }
+    // Tail: one chunk per lane at a time, the last possibly partial.
+    for (; c0 < c_end; c0 += 64) {
+        const int32_t c = c0 + lane;
+        if (c >= c_end) break;
+        const v4i v = src[c];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, v);
     }
 }
 
-template <int U, bool NT>
-hipError_t launch(const DispatchArgs& a, int32_t segments, int32_t seg_chunks,
-                  hipStream_t stream) {
+template <int K>
+hipError_t launch_k(const DispatchArgs& a, int32_t segments, int32_t seg_chunks,
+                    hipStream_t stream) {
     const int64_t items = int64_t(a.T) * segments;
     const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    hipLaunchKernelGGL((dispatch_kernel<U, NT>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kMoveThreads), 0, stream, static_cast<const v4i*>(a.x), a.scores,
-                       a.row_map, a.T, a.K, a.chunks, segments, seg_chunks, a.max_rows,
-                       static_cast<v4i*>(a.x_e), a.s_e);
+    auto kernel = a.nontemporal ? dispatch_kernel<K, true> : dispatch_kernel<K, false>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kMoveThreads), 0,
+                       stream, static_cast<const v4i*>(a.x), a.scores, a.row_map, a.T,
+                       a.chunks, segments, seg_chunks, a.max_rows, static_cast<v4i*>(a.x_e),
+                       a.s_e);
     return hipGetLastError();
 }
 
@@ -103,8 +120,16 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
     if (a.T <= 0) return hipSuccess;
     const int32_t seg_chunks = segment_chunks(a.chunks, a.segments);
     const int32_t segments = (a.chunks + seg_chunks - 1) / seg_chunks;
-    return a.nontemporal ? launch<4, true>(a, segments, seg_chunks, stream)
-                         : launch<4, false>(a, segments, seg_chunks, stream);
+    switch (a.K) {
+#define MOE_DISPATCH_CASE(k) \
+    case k: return launch_k<k>(a, segments, seg_chunks, stream);
+        MOE_DISPATCH_CASE(1) MOE_DISPATCH_CASE(2) MOE_DISPATCH_CASE(3) MOE_DISPATCH_CASE(4)
+        MOE_DISPATCH_CASE(5) MOE_DISPATCH_CASE(6) MOE_DISPATCH_CASE(7) MOE_DISPATCH_CASE(8)
+        MOE_DISPATCH_CASE(9) MOE_DISPATCH_CASE(10) MOE_DISPATCH_CASE(11) MOE_DISPATCH_CASE(12)
+        MOE_DISPATCH_CASE(13) MOE_DISPATCH_CASE(14) MOE_DISPATCH_CASE(15) MOE_DISPATCH_CASE(16)
+#undef MOE_DISPATCH_CASE
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moe

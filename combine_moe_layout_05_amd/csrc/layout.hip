@@ -13,15 +13,15 @@
 //                    or -1 (no expert, or padding t >= T)
 //   src_map[row]   = t*K+k
 //
-// Three launches, no atomics on global memory and no host round trip:
+// Two launches, no atomics on global memory and no host round trip:
 //   1. count: each workgroup histograms a 1024-slot tile into LDS and writes
 //      its row of block_hist[tile][e].
-//   2. scan: one workgroup; thread e scans block_hist[.][e] over tiles into
-//      block_base (exclusive, per expert) and then the workgroup scans the
-//      per-expert totals into offsets.
-//   3. rank: each workgroup re-reads its tile and ranks every slot among the
-//      earlier slots of the same expert; the order is fixed by the slot
-//      index alone, so the result is deterministic under any skew.
+//   2. rank: each workgroup first turns the tile histograms into the global
+//      offsets (sum over all tiles, exclusive scan over experts) and its own
+//      per-expert base (sum over earlier tiles); workgroup 0 also writes
+//      counts and offsets. It then re-reads its tile and ranks every slot
+//      among the earlier slots of the same expert. The order is fixed by the
+//      slot index alone, so the result is deterministic under any skew.
 // Within a wavefront, slots with the same expert are found with a ballot per
 // expert-id bit (a lane's peers are the lanes whose id agrees on every bit);
 // the lowest peer updates the wavefront's LDS histogram once per group, so a
@@ -83,77 +83,76 @@ void layout_count_kernel(const int32_t* __restrict__ ids, int64_t nvalid,
     for (int e = tid; e < E; e += kLayoutThreads) out[e] = hist[e];
 }
 
-__global__ __launch_bounds__(kScanThreads)
-void layout_scan_kernel(const int32_t* __restrict__ block_hist, int32_t tiles, int32_t E,
-                        int32_t* __restrict__ block_base, int32_t* __restrict__ counts,
-                        int32_t* __restrict__ offsets) {
-    __shared__ int32_t wave_sum[kScanThreads / 64];
-    const int e = threadIdx.x;
-    const int lane = e & 63;
-    const int wave = e >> 6;
+// Experts owned by one thread in the offset computation (consecutive).
+constexpr int kExpertsPerThread = kMaxExperts / kLayoutThreads;
 
-    // Per expert, exclusive scan over tiles (tile order = slot order).
-    int32_t run = 0;
-    if (e < E) {
-        int32_t b = 0;
-        for (; b + 8 <= tiles; b += 8) {
-            int32_t v[8];
+__global__ __launch_bounds__(kLayoutThreads)
+void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t nslots,
+                        int32_t E, int bits, int32_t tiles,
+                        const int32_t* __restrict__ block_hist, int32_t* __restrict__ counts,
+                        int32_t* __restrict__ offsets, int32_t* __restrict__ row_map,
+                        int32_t* __restrict__ src_map) {
+    __shared__ int32_t wave_hist[kLayoutWaves][kMaxExperts];
+    __shared__ int32_t tile_first[kMaxExperts];
+    __shared__ int32_t wave_sum[kLayoutWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int32_t blk = static_cast<int32_t>(blockIdx.x);
+
+    // Per expert: total over all tiles and the part in tiles before this one.
+    const int e0 = tid * kExpertsPerThread;
+    int32_t tot[kExpertsPerThread];
+    int32_t pre[kExpertsPerThread];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = block_hist[int64_t(b + u) * E + e];
+    for (int j = 0; j < kExpertsPerThread; ++j) tot[j] = pre[j] = 0;
+    if (e0 < E) {
+#pragma unroll 4
+        for (int32_t b = 0; b < tiles; ++b) {
+            const int32_t* h = block_hist + int64_t(b) * E + e0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                block_base[int64_t(b + u) * E + e] = run;
-                run += v[u];
+            for (int j = 0; j < kExpertsPerThread; ++j) {
+                const int32_t v = (e0 + j < E) ? h[j] : 0;
+                tot[j] += v;
+                pre[j] += (b < blk) ? v : 0;
             }
         }
-        for (; b < tiles; ++b) {
-            const int32_t v = block_hist[int64_t(b) * E + e];
-            block_base[int64_t(b) * E + e] = run;
-            run += v;
-        }
     }
-
-    // Inclusive scan of the per-expert totals across the workgroup.
-    int32_t incl = run;
+    // Exclusive scan of the totals over experts (thread order = expert order).
+    int32_t mine_sum = 0;
+#pragma unroll
+    for (int j = 0; j < kExpertsPerThread; ++j) mine_sum += tot[j];
+    int32_t incl = mine_sum;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
         const int32_t up = __shfl_up(incl, d, 64);
         if (lane >= d) incl += up;
     }
     if (lane == 63) wave_sum[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        int32_t w = lane < kScanThreads / 64 ? wave_sum[lane] : 0;
-#pragma unroll
-        for (int d = 1; d < kScanThreads / 64; d <<= 1) {
-            const int32_t up = __shfl_up(w, d, 64);
-            if (lane >= d) w += up;
-        }
-        if (lane < kScanThreads / 64) wave_sum[lane] = w;
-    }
-    __syncthreads();
-    if (wave > 0) incl += wave_sum[wave - 1];
-    if (e < E) {
-        counts[e] = run;
-        offsets[e] = incl - run;
-        if (e == E - 1) offsets[E] = incl;
-    }
-}
-
-__global__ __launch_bounds__(kLayoutThreads)
-void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t nslots,
-                        int32_t E, int bits, const int32_t* __restrict__ offsets,
-                        const int32_t* __restrict__ block_base,
-                        int32_t* __restrict__ row_map, int32_t* __restrict__ src_map) {
-    __shared__ int32_t wave_hist[kLayoutWaves][kMaxExperts];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
     for (int e = tid; e < E; e += kLayoutThreads) {
 #pragma unroll
         for (int w = 0; w < kLayoutWaves; ++w) wave_hist[w][e] = 0;
     }
     __syncthreads();
+    int32_t run = incl - mine_sum;
+    for (int w = 0; w < wave; ++w) run += wave_sum[w];
+#pragma unroll
+    for (int j = 0; j < kExpertsPerThread; ++j) {
+        const int e = e0 + j;
+        if (e < E) {
+            tile_first[e] = run + pre[j];
+            if (blk == 0) {
+                counts[e] = tot[j];
+                offsets[e] = run;
+            }
+        }
+        run += tot[j];
+    }
+    if (blk == 0 && tid == kLayoutThreads - 1) {
+        int32_t total = 0;
+        for (int w = 0; w < kLayoutWaves; ++w) total += wave_sum[w];
+        offsets[E] = total;
+    }
 
     const int64_t base = int64_t(blockIdx.x) * kLayoutTile + wave * (64 * kLayoutSlotsPerLane);
     int32_t ex[kLayoutSlotsPerLane];
@@ -179,9 +178,8 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
     __syncthreads();
 
     // Turn the per-wavefront counts into each wavefront's first row per expert.
-    const int32_t* tile_base = block_base + int64_t(blockIdx.x) * E;
     for (int e = tid; e < E; e += kLayoutThreads) {
-        int32_t run = offsets[e] + tile_base[e];
+        int32_t run = tile_first[e];
 #pragma unroll
         for (int w = 0; w < kLayoutWaves; ++w) {
             const int32_t c = wave_hist[w][e];
@@ -216,21 +214,16 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(layout_count_kernel, dim3(static_cast<uint32_t>(tiles)),
                            dim3(kLayoutThreads), 0, stream, a.ids, a.nvalid, a.E, bits,
                            a.block_hist);
-        hipError_t err = hipGetLastError();
+        const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                       a.block_hist, static_cast<int32_t>(tiles), a.E, a.block_base,
-                       a.counts, a.offsets);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    if (tiles > 0) {
-        hipLaunchKernelGGL(layout_rank_kernel, dim3(static_cast<uint32_t>(tiles)),
-                           dim3(kLayoutThreads), 0, stream, a.ids, a.nvalid, a.nslots, a.E,
-                           bits, a.offsets, a.block_base, a.row_map, a.src_map);
-        err = hipGetLastError();
-    }
-    return err;
+    // At least one workgroup, so counts and offsets are written even for an
+    // empty capacity.
+    const uint32_t grid = static_cast<uint32_t>(tiles > 0 ? tiles : 1);
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(grid), dim3(kLayoutThreads), 0, stream, a.ids,
+                       a.nvalid, a.nslots, a.E, bits, static_cast<int32_t>(tiles), a.block_hist,
+                       a.counts, a.offsets, a.row_map, a.src_map);
+    return hipGetLastError();
 }
 
 }  // namespace moe

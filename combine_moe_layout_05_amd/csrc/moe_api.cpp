@@ -80,7 +80,6 @@ void plan(const moe_config* cfg, moe_buffers_desc* d) {
     d->counts = take(E * 4);
     d->offsets = take((E + 1) * 4);
     d->block_hist = take(d->max_tiles * E * 4);
-    d->block_base = take(d->max_tiles * E * 4);
     d->row_map = take(d->max_rows * 4);
     d->src_map = take(d->max_rows * 4);
     d->s_e = take(d->max_rows * 4);
@@ -185,12 +184,17 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     c->has_layout = false;
     c->layout_T = -1;
     c->layout_ntpr4 = -1;
-    // Defaults: split long rows so a workgroup's 4 wavefronts share one token's
-    // row; short rows keep one wavefront per token.
-    const int32_t seg = c->chunks >= 512 ? 2 : 1;
+    // Defaults from measurement on MI355X: one 16-byte chunk per lane per
+    // wavefront (a row of up to 16 KiB becomes up to 16 wavefront items, so
+    // a 4096-token batch of 14 KiB rows launches 57344 wavefronts), ordinary
+    // stores in dispatch and streaming loads in combine (the expert-output
+    // rows are read exactly once).
+    int32_t seg = (c->chunks + 63) / 64;
+    if (seg > moe::kMaxSegments) seg = moe::kMaxSegments;
     c->tuning.dispatch_segments = seg;
     c->tuning.combine_segments = seg;
     c->tuning.dispatch_nontemporal = 0;
+    c->tuning.combine_nontemporal = 1;
     *out = c;
     return MOE_OK;
 }
@@ -214,6 +218,7 @@ int moe_set_tuning(moe_ctx* ctx, const moe_tuning* t) {
     if (t->dispatch_segments) ctx->tuning.dispatch_segments = t->dispatch_segments;
     if (t->combine_segments) ctx->tuning.combine_segments = t->combine_segments;
     ctx->tuning.dispatch_nontemporal = t->dispatch_nontemporal ? 1 : 0;
+    ctx->tuning.combine_nontemporal = t->combine_nontemporal ? 1 : 0;
     return MOE_OK;
 }
 
@@ -237,7 +242,6 @@ int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
     a.nslots = ntpr4 * K;
     a.E = ctx->cfg.num_experts;
     a.block_hist = at<int32_t>(ctx, ctx->desc.block_hist);
-    a.block_base = at<int32_t>(ctx, ctx->desc.block_base);
     a.counts = at<int32_t>(ctx, ctx->desc.counts);
     a.offsets = at<int32_t>(ctx, ctx->desc.offsets);
     a.row_map = at<int32_t>(ctx, ctx->desc.row_map);
@@ -298,6 +302,7 @@ int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
     a.bf16 = ctx->cfg.dtype == MOE_BF16;
     a.y = at<void>(ctx, ctx->desc.y);
     a.segments = ctx->tuning.combine_segments;
+    a.nontemporal = ctx->tuning.combine_nontemporal != 0;
     if (moe::launch_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     *d_y_out = a.y;

@@ -15,7 +15,6 @@ constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / 64;
 constexpr int kLayoutSlotsPerLane = 4;
 constexpr int kLayoutTile = kLayoutThreads * kLayoutSlotsPerLane;
-constexpr int kScanThreads = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
 
@@ -24,6 +23,8 @@ constexpr int kMaxTopk = 16;
 constexpr int kMoveThreads = 256;
 constexpr int kMoveWaves = kMoveThreads / 64;
 constexpr int kMaxSegments = 16;
+
+static_assert(kMaxExperts % kLayoutThreads == 0, "experts split evenly over layout threads");
 
 // Number of layout tiles covering n slots.
 inline int64_t layout_tiles(int64_t slots) {
@@ -51,7 +52,6 @@ struct LayoutArgs {
     int64_t nslots;         // round_up4(ntpr)*K slots written to row_map
     int32_t E;
     int32_t* block_hist;    // [tiles][E]
-    int32_t* block_base;    // [tiles][E]
     int32_t* counts;        // [E]
     int32_t* offsets;       // [E+1]
     int32_t* row_map;       // [nslots]
@@ -85,6 +85,7 @@ struct CombineArgs {
     bool bf16;
     void* y;                // [T][row_bytes]
     int32_t segments;
+    bool nontemporal;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

@@ -187,12 +187,15 @@ class MoeDispatcher:
 
     # -- tuning ------------------------------------------------------------
     def set_tuning(self, dispatch_segments: int = 0, combine_segments: int = 0,
-                   dispatch_nontemporal: bool = False) -> None:
-        t = L.MoeTuning(dispatch_segments, combine_segments, int(dispatch_nontemporal))
+                   dispatch_nontemporal: bool = False, combine_nontemporal: bool = False) -> None:
+        """Launch shape only; results never depend on it."""
+        t = L.MoeTuning(dispatch_segments, combine_segments, int(dispatch_nontemporal),
+                        int(combine_nontemporal))
         L.check(self._lib.moe_set_tuning(self._ctx, C.byref(t)), "moe_set_tuning")
 
     def get_tuning(self) -> dict:
         t = L.MoeTuning()
         L.check(self._lib.moe_get_tuning(self._ctx, C.byref(t)), "moe_get_tuning")
         return {"dispatch_segments": t.dispatch_segments, "combine_segments": t.combine_segments,
-                "dispatch_nontemporal": bool(t.dispatch_nontemporal)}
+                "dispatch_nontemporal": bool(t.dispatch_nontemporal),
+                "combine_nontemporal": bool(t.combine_nontemporal)}
