@@ -45,6 +45,8 @@ def parse_args():
     p.add_argument("--workload", default="dsv3")
     p.add_argument("--cold-iters", type=int, default=10,
                    help="iterations of the cache-flushed per-kernel measurement (0 = skip)")
+    p.add_argument("--graph-replays", type=int, default=20,
+                   help="timed replays of the step captured in a hipGraph (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget of the oracle CPU baseline (0 = skip)")
     p.add_argument("--dispatch-segments", type=int, default=0)
@@ -53,6 +55,8 @@ def parse_args():
                    help="1/0 forces dispatch's streaming stores on/off; -1 keeps the default")
     p.add_argument("--combine-nontemporal", type=int, default=-1,
                    help="1/0 forces combine's streaming loads on/off; -1 keeps the default")
+    p.add_argument("--dispatch-block-waves", type=int, default=0)
+    p.add_argument("--combine-block-waves", type=int, default=0)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run plain device write/read/copy of this size (HBM ceiling, "
                         "counter scaling)")
@@ -157,12 +161,10 @@ def main() -> int:
     ids = torch.from_numpy(b["ids"]).to(dev)
     s = torch.from_numpy(b["scores"]).to(dev)
     disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=dev)
-    cur = disp.get_tuning()
     disp.set_tuning(args.dispatch_segments, args.combine_segments,
-                    bool(args.dispatch_nontemporal) if args.dispatch_nontemporal >= 0
-                    else cur["dispatch_nontemporal"],
-                    bool(args.combine_nontemporal) if args.combine_nontemporal >= 0
-                    else cur["combine_nontemporal"])
+                    bool(args.dispatch_nontemporal) if args.dispatch_nontemporal >= 0 else None,
+                    bool(args.combine_nontemporal) if args.combine_nontemporal >= 0 else None,
+                    args.dispatch_block_waves, args.combine_block_waves)
     tuning = disp.get_tuning()
     ntpr = w.ntpr
 
@@ -207,21 +209,47 @@ def main() -> int:
         f"dispatch {avg['dispatch'] * 1e3:.1f} us ({gbps['dispatch']:.0f} GB/s), "
         f"combine {avg['combine'] * 1e3:.1f} us ({gbps['combine']:.0f} GB/s)")
 
-    # Cold-cache per-kernel times: a 1 GiB write evicts L2 and the MALL
-    # before each timed kernel (outside the timed interval).
+    # The same step captured once into a hipGraph and replayed: the launch
+    # gaps between the kernels disappear.
+    graph_us = None
+    if args.graph_replays > 0:
+        log(f"graph capture of one step, {args.graph_replays} timed replays")
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t_g = time.perf_counter()
+        for _ in range(args.graph_replays):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t_g) * 1e6 / args.graph_replays
+        del g
+        log(f"graph replay {graph_us:.1f} us per step")
+
+    # Cold-cache per-kernel times: a 1 GiB read evicts L2 and the MALL
+    # before each timed kernel (outside the timed interval); a read leaves
+    # clean lines, so no write-back of the flush lands in the timed kernel.
     cold = None
     if args.cold_iters > 0:
         log(f"cold-cache per-kernel timing, {args.cold_iters} iterations")
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         cd, cc = [], []
         for i in range(args.cold_iters):
             lay = disp.layout(ids, ntpr)
-            scratch.fill_(i & 0xFF)
+            torch.sum(scratch, dim=0, out=sink)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
             e1.record()
-            scratch.fill_((i + 1) & 0xFF)
+            torch.sum(scratch, dim=0, out=sink)
             e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e2.record()
             disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
@@ -292,6 +320,7 @@ def main() -> int:
             "frac_of_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "cold_cache": cold,
+        "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
     }
     print(json.dumps(out), flush=True)
     return 0

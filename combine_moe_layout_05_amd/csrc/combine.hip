@@ -12,13 +12,18 @@
 // computed; padding rows are never materialized.
 //
 // Bound by HBM reads (K rows read per row written). One wavefront per
-// (token, row segment); each lane owns one 16-byte chunk per iteration and
-// issues its K row loads back to back. When every slot of the token has an
-// expert (the common case) the loop is double-buffered: the next chunk's K
-// loads are issued before the current chunk is reduced and stored, and no
-// per-slot branch sits between loads and their use. Otherwise no-expert slots
-// load the token's first valid row instead (always written, finite) and skip
-// it in the sum, which keeps every load unconditional.
+// (token, row segment); the workgroup's row-map entries and scores are staged
+// in LDS with one coalesced load and each wavefront moves its token's K rows
+// and scores into SGPRs. Each lane owns one 16-byte chunk per iteration and
+// issues its K row loads
+// back to back, as streaming loads by default (each row is read once). With
+// the default launch shape a segment is exactly one chunk per lane, so a
+// wavefront is: K loads, K fused multiply-adds per element, one store. For
+// longer segments, when every slot of the token has an expert, the loop is
+// double-buffered: the next chunk's K loads are issued before the current
+// chunk is reduced and stored. No-expert slots load the token's first valid
+// row instead (always written, finite) and skip it in the sum, which keeps
+// every load unconditional.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -84,26 +89,32 @@ __device__ __forceinline__ v4i fetch(const v4i* p) {
         return *p;
 }
 
-template <int K, bool BF16, bool NT>
-__global__ __launch_bounds__(kMoveThreads)
+// One wavefront per (token, row segment). SINGLE: the segment is exactly one
+// 16-byte chunk per lane, so no loop and no second buffer (fewer registers,
+// more wavefronts resident); otherwise the segment is walked chunk by chunk.
+template <int K, bool BF16, bool NT, bool SINGLE>
+__global__ __launch_bounds__(kMaxBlockThreads)
 void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row_map,
                     const float* __restrict__ scores, int32_t T, int32_t chunks,
                     int32_t segments, int32_t seg_chunks, int64_t row_limit,
                     v4i* __restrict__ y) {
     using L = Lanes<BF16>;
-    __shared__ int32_t tile_rows[kMoveWaves * K];
-    __shared__ float tile_scores[kMoveWaves * K];
+    // Row-map entries and scores of the workgroup's tokens: one coalesced load
+    // into LDS, then a barrier. Rows outside [0, row_limit) count as no
+    // expert, and such a slot's score is never loaded.
+    __shared__ int32_t tile_rows[kMaxBlockWaves * K];
+    __shared__ float tile_scores[kMaxBlockWaves * K];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-
-    const int64_t item0 = int64_t(blockIdx.x) * kMoveWaves;
+    const int block_waves = static_cast<int>(blockDim.x) >> 6;
+    const int64_t item0 = int64_t(blockIdx.x) * block_waves;
     const int64_t t_first = item0 / segments;
-    int64_t t_last = (item0 + kMoveWaves - 1) / segments;
+    int64_t t_last = (item0 + block_waves - 1) / segments;
     if (t_last > int64_t(T) - 1) t_last = int64_t(T) - 1;
     const int staged = static_cast<int>(t_last - t_first + 1) * K;
     if (tid < staged) {
-        int32_t r = row_map[t_first * K + tid];
+        const int32_t r = row_map[t_first * K + tid];
         const bool ok = r >= 0 && r < row_limit;
         tile_rows[tid] = ok ? r : -1;
         tile_scores[tid] = ok ? scores[t_first * K + tid] : 0.0f;
@@ -123,14 +134,14 @@ void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         row[k] = __builtin_amdgcn_readfirstlane(tile_rows[lt * K + k]);
-        s[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tile_scores[lt * K + k])));
+        s[k] = __int_as_float(
+            __builtin_amdgcn_readfirstlane(__float_as_int(tile_scores[lt * K + k])));
         if (fallback < 0 && row[k] >= 0) fallback = row[k];
         all_valid = all_valid && row[k] >= 0;
     }
 
     const int32_t c_begin = seg * seg_chunks;
     const int32_t c_end = min(c_begin + seg_chunks, chunks);
-    const int32_t iters = (c_end - c_begin + 63) / 64;   // one chunk per lane each
     v4i* dst = y + t * chunks;
 
     if (fallback < 0) {  // no slot reaches an expert: +0.0
@@ -143,53 +154,60 @@ void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row
 #pragma unroll
     for (int k = 0; k < K; ++k) src[k] = y_e + int64_t(row[k] >= 0 ? row[k] : fallback) * chunks;
 
-    // Chunk of iteration i for this lane; the last iteration's lanes past
-    // the segment end re-load its last chunk and do not store.
-    auto chunk_of = [&](int32_t i) { return min(c_begin + i * 64 + lane, c_end - 1); };
-    auto load = [&](v4i (&b)[K], int32_t i) {
-        const int32_t c = chunk_of(i);
-#pragma unroll
-        for (int k = 0; k < K; ++k) b[k] = fetch<NT>(src[k] + c);
-    };
-
-    if (all_valid) {
-        // Every slot has an expert: no per-slot test, loads of the next chunk
-        // are in flight while this one is reduced and stored.
-        auto emit = [&](const v4i (&b)[K], int32_t i) {
-            float acc[L::N];
-#pragma unroll
-            for (int e = 0; e < L::N; ++e) acc[e] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < K; ++k) L::fma_into(acc, s[k], b[k]);
-            const int32_t c = c_begin + i * 64 + lane;
-            if (c < c_end) dst[c] = L::pack(acc);
-        };
-        v4i b0[K], b1[K];
-        load(b0, 0);
-        int32_t i = 0;
-        for (; i + 1 < iters; i += 2) {
-            load(b1, i + 1);
-            emit(b0, i);
-            load(b0, min(i + 2, iters - 1));
-            emit(b1, i + 1);
-        }
-        if (i < iters) emit(b0, i);
-        return;
-    }
-
-    // Some slots without an expert: they are skipped (their loaded data and
-    // score never enter the sum).
-    for (int32_t i = 0; i < iters; ++i) {
-        v4i b[K];
-        load(b, i);
+    // Reduce one loaded chunk: every slot, or only the slots with an expert.
+    auto reduce = [&](const v4i (&b)[K], bool every) {
         float acc[L::N];
 #pragma unroll
         for (int e = 0; e < L::N; ++e) acc[e] = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k)
-            if (row[k] >= 0) L::fma_into(acc, s[k], b[k]);
-        const int32_t c = c_begin + i * 64 + lane;
-        if (c < c_end) dst[c] = L::pack(acc);
+            if (every || row[k] >= 0) L::fma_into(acc, s[k], b[k]);
+        return L::pack(acc);
+    };
+
+    if constexpr (SINGLE) {
+        // Lanes past the segment end (a short last segment) load its last
+        // chunk and do not store.
+        const int32_t c = c_begin + lane;
+        const int32_t cl = min(c, c_end - 1);
+        v4i b[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) b[k] = fetch<NT>(src[k] + cl);
+        const v4i out = all_valid ? reduce(b, true) : reduce(b, false);
+        if (c < c_end) dst[c] = out;
+        return;
+    } else {
+        const int32_t iters = (c_end - c_begin + 63) / 64;   // one chunk per lane each
+        auto load = [&](v4i (&b)[K], int32_t i) {
+            const int32_t c = min(c_begin + i * 64 + lane, c_end - 1);
+#pragma unroll
+            for (int k = 0; k < K; ++k) b[k] = fetch<NT>(src[k] + c);
+        };
+        auto emit = [&](const v4i (&b)[K], int32_t i, bool every) {
+            const v4i out = reduce(b, every);
+            const int32_t c = c_begin + i * 64 + lane;
+            if (c < c_end) dst[c] = out;
+        };
+        if (all_valid) {
+            // Every slot has an expert: the next chunk's loads are in flight
+            // while this one is reduced and stored.
+            v4i b0[K], b1[K];
+            load(b0, 0);
+            int32_t i = 0;
+            for (; i + 1 < iters; i += 2) {
+                load(b1, i + 1);
+                emit(b0, i, true);
+                load(b0, min(i + 2, iters - 1));
+                emit(b1, i + 1, true);
+            }
+            if (i < iters) emit(b0, i, true);
+            return;
+        }
+        for (int32_t i = 0; i < iters; ++i) {
+            v4i b[K];
+            load(b, i);
+            emit(b, i, false);
+        }
     }
 }
 
@@ -197,9 +215,13 @@ template <int K, bool BF16>
 hipError_t launch_k(const CombineArgs& a, int32_t segments, int32_t seg_chunks,
                     hipStream_t stream) {
     const int64_t items = int64_t(a.T) * segments;
-    const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    auto kernel = a.nontemporal ? combine_kernel<K, BF16, true> : combine_kernel<K, BF16, false>;
-    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kMoveThreads), 0, stream,
+    const int64_t blocks = (items + a.block_waves - 1) / a.block_waves;
+    const bool single = seg_chunks == 64;
+    auto kernel = a.nontemporal ? (single ? combine_kernel<K, BF16, true, true>
+                                          : combine_kernel<K, BF16, true, false>)
+                                : (single ? combine_kernel<K, BF16, false, true>
+                                          : combine_kernel<K, BF16, false, false>);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * a.block_waves), 0, stream,
                        static_cast<const v4i*>(a.y_e), a.row_map, a.scores, a.T, a.chunks,
                        segments, seg_chunks, a.row_limit, static_cast<v4i*>(a.y));
     return hipGetLastError();

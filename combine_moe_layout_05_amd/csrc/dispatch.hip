@@ -14,10 +14,14 @@
 // The work is pure data movement bound by HBM writes (K row writes per row
 // read). One wavefront takes one (token, row segment) item: it loads the
 // segment once, 16 bytes per lane so each wavefront access is a contiguous
-// 1 KiB run, and stores it K times. The workgroup's row-map entries (at most
-// 4 tokens x K) are staged in LDS with one coalesced load and moved into
-// SGPRs once per wavefront, so the K destination row addresses are scalar
-// and the per-slot "has an expert" test is a scalar branch.
+// 1 KiB run, and stores it K times. With the default launch shape a segment
+// is exactly one 16-byte chunk per lane, so a workgroup's wavefronts cover
+// neighbouring 1 KiB pieces of one token row. The workgroup's row-map entries
+// are staged in LDS with one coalesced load; each wavefront moves its K rows
+// into SGPRs, so destination addresses are scalar and the per-slot "has an
+// expert" test is a scalar branch. (Measured on MI355X: staging behind a
+// workgroup barrier beats per-wavefront scalar loads of the row map by ~9 %,
+// because the barrier lines the wavefronts up on neighbouring pieces.)
 #include "moe_kernels.h"
 
 namespace moe {
@@ -35,21 +39,27 @@ __device__ __forceinline__ void put(v4i* p, v4i v) {
         *p = v;
 }
 
-template <int K, bool NT>
-__global__ __launch_bounds__(kMoveThreads)
+// One wavefront per (token, row segment). SINGLE: the segment is exactly one
+// 16-byte chunk per lane (the default launch shape); otherwise the segment is
+// copied in groups of U chunks per lane, then one chunk at a time.
+template <int K, bool NT, bool SINGLE>
+__global__ __launch_bounds__(kMaxBlockThreads)
 void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores,
                      const int32_t* __restrict__ row_map, int32_t T, int32_t chunks,
                      int32_t segments, int32_t seg_chunks, int64_t max_rows,
                      v4i* __restrict__ x_e, float* __restrict__ s_e) {
     constexpr int U = kDispatchUnroll;
-    __shared__ int32_t tile_rows[kMoveWaves * K];
+    // Row-map entries of the workgroup's tokens: one coalesced load, then a
+    // barrier. The barrier also starts the workgroup's wavefronts together, so
+    // they store neighbouring 1 KiB pieces of the same rows at the same time.
+    __shared__ int32_t tile_rows[kMaxBlockWaves * K];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-
-    const int64_t item0 = int64_t(blockIdx.x) * kMoveWaves;
+    const int block_waves = static_cast<int>(blockDim.x) >> 6;
+    const int64_t item0 = int64_t(blockIdx.x) * block_waves;
     const int64_t t_first = item0 / segments;
-    int64_t t_last = (item0 + kMoveWaves - 1) / segments;
+    int64_t t_last = (item0 + block_waves - 1) / segments;
     if (t_last > int64_t(T) - 1) t_last = int64_t(T) - 1;
     const int staged = static_cast<int>(t_last - t_first + 1) * K;
     if (tid < staged) {
@@ -62,42 +72,59 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     const int64_t t = item / segments;
     if (t >= T) return;
     const int seg = static_cast<int>(item - t * segments);
-    const int lt = static_cast<int>(t - t_first);
-
+    const int32_t* rows = tile_rows + (t - t_first) * K;
     int32_t row[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) row[k] = __builtin_amdgcn_readfirstlane(tile_rows[lt * K + k]);
-
-    if (seg == 0 && lane < K) {
-        const int32_t r = tile_rows[lt * K + lane];
-        if (r >= 0) s_e[r] = scores[t * K + lane];
-    }
+    for (int k = 0; k < K; ++k) row[k] = __builtin_amdgcn_readfirstlane(rows[k]);
 
     const int32_t c_begin = seg * seg_chunks;
     const int32_t c_end = min(c_begin + seg_chunks, chunks);
     const v4i* src = x + t * chunks;
-    int32_t c0 = c_begin;
-    // Whole groups: every lane has U chunks in range.
-    for (; c0 + 64 * U <= c_end; c0 += 64 * U) {
-        v4i v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = src[c0 + u * 64 + lane];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (row[k] < 0) continue;
-            v4i* dst = x_e + int64_t(row[k]) * chunks + c0 + lane;
-#pragma unroll
-            for (int u = 0; u < U; ++u) put<NT>(dst + u * 64, v[u]);
+
+    // Lane k < K of the first segment also moves slot k's score.
+    auto move_score = [&]() {
+        if (seg == 0 && lane < K) {
+            const int32_t r = rows[lane];
+            if (r >= 0) s_e[r] = scores[t * K + lane];
         }
-    }
-    // Tail: one chunk per lane at a time, the last possibly partial.
-    for (; c0 < c_end; c0 += 64) {
-        const int32_t c = c0 + lane;
-        if (c >= c_end) break;
-        const v4i v = src[c];
+    };
+
+    if constexpr (SINGLE) {
+        const int32_t c = c_begin + lane;
+        const bool in = c < c_end;
+        v4i v;
+        if (in) v = src[c];
+        move_score();
+        if (in) {
 #pragma unroll
-        for (int k = 0; k < K; ++k)
-            if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, v);
+            for (int k = 0; k < K; ++k)
+                if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, v);
+        }
+    } else {
+        move_score();
+        int32_t c0 = c_begin;
+        // Whole groups: every lane has U chunks in range.
+        for (; c0 + 64 * U <= c_end; c0 += 64 * U) {
+            v4i v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = src[c0 + u * 64 + lane];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (row[k] < 0) continue;
+                v4i* dst = x_e + int64_t(row[k]) * chunks + c0 + lane;
+#pragma unroll
+                for (int u = 0; u < U; ++u) put<NT>(dst + u * 64, v[u]);
+            }
+        }
+        // Tail: one chunk per lane at a time, the last possibly partial.
+        for (; c0 < c_end; c0 += 64) {
+            const int32_t c = c0 + lane;
+            if (c >= c_end) break;
+            const v4i v = src[c];
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, v);
+        }
     }
 }
 
@@ -105,9 +132,13 @@ template <int K>
 hipError_t launch_k(const DispatchArgs& a, int32_t segments, int32_t seg_chunks,
                     hipStream_t stream) {
     const int64_t items = int64_t(a.T) * segments;
-    const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    auto kernel = a.nontemporal ? dispatch_kernel<K, true> : dispatch_kernel<K, false>;
-    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kMoveThreads), 0,
+    const int64_t blocks = (items + a.block_waves - 1) / a.block_waves;
+    const bool single = seg_chunks == 64;
+    auto kernel = a.nontemporal ? (single ? dispatch_kernel<K, true, true>
+                                          : dispatch_kernel<K, true, false>)
+                                : (single ? dispatch_kernel<K, false, true>
+                                          : dispatch_kernel<K, false, false>);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * a.block_waves), 0,
                        stream, static_cast<const v4i*>(a.x), a.scores, a.row_map, a.T,
                        a.chunks, segments, seg_chunks, a.max_rows, static_cast<v4i*>(a.x_e),
                        a.s_e);

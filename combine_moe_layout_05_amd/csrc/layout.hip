@@ -55,14 +55,16 @@ __device__ __forceinline__ int32_t slot_expert(const int32_t* __restrict__ ids,
     return (static_cast<uint32_t>(e) < static_cast<uint32_t>(E)) ? e : -1;
 }
 
+// Histogram rows are padded to E4 = round_up(E, 4) entries (zeros past E) so
+// they can be read as 16-byte vectors.
 __global__ __launch_bounds__(kLayoutThreads)
 void layout_count_kernel(const int32_t* __restrict__ ids, int64_t nvalid,
-                         int32_t E, int bits, int32_t* __restrict__ block_hist) {
+                         int32_t E, int32_t E4, int bits, int32_t* __restrict__ block_hist) {
     __shared__ int32_t hist[kMaxExperts];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    for (int e = tid; e < E; e += kLayoutThreads) hist[e] = 0;
+    for (int e = tid; e < E4; e += kLayoutThreads) hist[e] = 0;
     __syncthreads();
 
     const int64_t base = int64_t(blockIdx.x) * kLayoutTile + wave * (64 * kLayoutSlotsPerLane);
@@ -79,44 +81,75 @@ void layout_count_kernel(const int32_t* __restrict__ ids, int64_t nvalid,
         if (valid && (peers & below) == 0) atomicAdd(&hist[ex[j]], __popcll(peers));
     }
     __syncthreads();
-    int32_t* out = block_hist + int64_t(blockIdx.x) * E;
-    for (int e = tid; e < E; e += kLayoutThreads) out[e] = hist[e];
+    int32_t* out = block_hist + int64_t(blockIdx.x) * E4;
+    for (int e = tid; e < E4; e += kLayoutThreads) out[e] = hist[e];
 }
 
-// Experts owned by one thread in the offset computation (consecutive).
+// Experts owned by one thread in the offset scan (consecutive).
 constexpr int kExpertsPerThread = kMaxExperts / kLayoutThreads;
+// At most this many threads share one quad of experts in the tile sums.
+constexpr int kMaxSlices = 16;
+typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kLayoutThreads)
 void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t nslots,
-                        int32_t E, int bits, int32_t tiles,
+                        int32_t E, int32_t E4, int bits, int32_t tiles,
                         const int32_t* __restrict__ block_hist, int32_t* __restrict__ counts,
                         int32_t* __restrict__ offsets, int32_t* __restrict__ row_map,
                         int32_t* __restrict__ src_map) {
     __shared__ int32_t wave_hist[kLayoutWaves][kMaxExperts];
     __shared__ int32_t tile_first[kMaxExperts];
+    __shared__ int32_t part_tot[kMaxExperts];
+    __shared__ int32_t part_pre[kMaxExperts];
     __shared__ int32_t wave_sum[kLayoutWaves];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int32_t blk = static_cast<int32_t>(blockIdx.x);
 
-    // Per expert: total over all tiles and the part in tiles before this one.
+    // Per expert: the total over all tiles and the part in tiles before this
+    // one. Thread (quad q, slice sl) sums experts 4q..4q+3 over tiles
+    // sl, sl+S, ... with 16-byte loads; the S slices of a quad are then added
+    // in LDS (integer adds, so the order does not matter).
+    const int quads = E4 / 4;
+    int S = kLayoutThreads / quads;
+    if (S > kMaxSlices) S = kMaxSlices;
+    for (int e = tid; e < E4; e += kLayoutThreads) {
+        part_tot[e] = 0;
+        part_pre[e] = 0;
+#pragma unroll
+        for (int w = 0; w < kLayoutWaves; ++w) wave_hist[w][e] = 0;
+    }
+    __syncthreads();
+    {
+        const int q = tid % quads;
+        const int sl = tid / quads;
+        if (sl < S) {
+            v4i tot4 = {0, 0, 0, 0};
+            v4i pre4 = {0, 0, 0, 0};
+            const v4i* h = reinterpret_cast<const v4i*>(block_hist) + q;
+#pragma unroll 8
+            for (int32_t b = sl; b < tiles; b += S) {
+                const v4i v = h[int64_t(b) * quads];
+                tot4 += v;
+                if (b < blk) pre4 += v;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (tot4[j]) atomicAdd(&part_tot[4 * q + j], tot4[j]);
+                if (pre4[j]) atomicAdd(&part_pre[4 * q + j], pre4[j]);
+            }
+        }
+    }
+    __syncthreads();
     const int e0 = tid * kExpertsPerThread;
     int32_t tot[kExpertsPerThread];
     int32_t pre[kExpertsPerThread];
 #pragma unroll
-    for (int j = 0; j < kExpertsPerThread; ++j) tot[j] = pre[j] = 0;
-    if (e0 < E) {
-#pragma unroll 4
-        for (int32_t b = 0; b < tiles; ++b) {
-            const int32_t* h = block_hist + int64_t(b) * E + e0;
-#pragma unroll
-            for (int j = 0; j < kExpertsPerThread; ++j) {
-                const int32_t v = (e0 + j < E) ? h[j] : 0;
-                tot[j] += v;
-                pre[j] += (b < blk) ? v : 0;
-            }
-        }
+    for (int j = 0; j < kExpertsPerThread; ++j) {
+        const bool in = e0 + j < E4;
+        tot[j] = in ? part_tot[e0 + j] : 0;
+        pre[j] = in ? part_pre[e0 + j] : 0;
     }
     // Exclusive scan of the totals over experts (thread order = expert order).
     int32_t mine_sum = 0;
@@ -129,10 +162,6 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
         if (lane >= d) incl += up;
     }
     if (lane == 63) wave_sum[wave] = incl;
-    for (int e = tid; e < E; e += kLayoutThreads) {
-#pragma unroll
-        for (int w = 0; w < kLayoutWaves; ++w) wave_hist[w][e] = 0;
-    }
     __syncthreads();
     int32_t run = incl - mine_sum;
     for (int w = 0; w < wave; ++w) run += wave_sum[w];
@@ -210,9 +239,10 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     const int64_t tiles = layout_tiles(a.nslots);
     const int bits = expert_bits(a.E);
+    const int32_t E4 = padded_experts(a.E);
     if (tiles > 0) {
         hipLaunchKernelGGL(layout_count_kernel, dim3(static_cast<uint32_t>(tiles)),
-                           dim3(kLayoutThreads), 0, stream, a.ids, a.nvalid, a.E, bits,
+                           dim3(kLayoutThreads), 0, stream, a.ids, a.nvalid, a.E, E4, bits,
                            a.block_hist);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -221,7 +251,7 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     // empty capacity.
     const uint32_t grid = static_cast<uint32_t>(tiles > 0 ? tiles : 1);
     hipLaunchKernelGGL(layout_rank_kernel, dim3(grid), dim3(kLayoutThreads), 0, stream, a.ids,
-                       a.nvalid, a.nslots, a.E, bits, static_cast<int32_t>(tiles), a.block_hist,
+                       a.nvalid, a.nslots, a.E, E4, bits, static_cast<int32_t>(tiles), a.block_hist,
                        a.counts, a.offsets, a.row_map, a.src_map);
     return hipGetLastError();
 }

@@ -79,7 +79,7 @@ void plan(const moe_config* cfg, moe_buffers_desc* d) {
     };
     d->counts = take(E * 4);
     d->offsets = take((E + 1) * 4);
-    d->block_hist = take(d->max_tiles * E * 4);
+    d->block_hist = take(d->max_tiles * moe::padded_experts(static_cast<int32_t>(E)) * 4);
     d->row_map = take(d->max_rows * 4);
     d->src_map = take(d->max_rows * 4);
     d->s_e = take(d->max_rows * 4);
@@ -186,15 +186,21 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     c->layout_ntpr4 = -1;
     // Defaults from measurement on MI355X: one 16-byte chunk per lane per
     // wavefront (a row of up to 16 KiB becomes up to 16 wavefront items, so
-    // a 4096-token batch of 14 KiB rows launches 57344 wavefronts), ordinary
-    // stores in dispatch and streaming loads in combine (the expert-output
-    // rows are read exactly once).
+    // a 4096-token batch of 14 KiB rows launches 57344 wavefronts); dispatch
+    // workgroups hold one token's whole row (its wavefronts then store
+    // neighbouring pieces of the same rows together) and ordinary stores;
+    // combine uses 4-wavefront workgroups and streaming loads (the
+    // expert-output rows are read exactly once).
     int32_t seg = (c->chunks + 63) / 64;
     if (seg > moe::kMaxSegments) seg = moe::kMaxSegments;
+    const int32_t seg_eff =
+        (c->chunks + moe::segment_chunks(c->chunks, seg) - 1) / moe::segment_chunks(c->chunks, seg);
     c->tuning.dispatch_segments = seg;
     c->tuning.combine_segments = seg;
     c->tuning.dispatch_nontemporal = 0;
     c->tuning.combine_nontemporal = 1;
+    c->tuning.dispatch_block_waves = seg_eff >= 4 ? seg_eff : moe::kMaxBlockWaves;
+    c->tuning.combine_block_waves = 4;
     *out = c;
     return MOE_OK;
 }
@@ -213,10 +219,14 @@ int moe_workspace_offsets(const moe_ctx* ctx, moe_buffers_desc* out) {
 int moe_set_tuning(moe_ctx* ctx, const moe_tuning* t) {
     if (!ctx || !t) return MOE_ERR_INVALID_ARG;
     if (t->dispatch_segments < 0 || t->dispatch_segments > moe::kMaxSegments ||
-        t->combine_segments < 0 || t->combine_segments > moe::kMaxSegments)
+        t->combine_segments < 0 || t->combine_segments > moe::kMaxSegments ||
+        t->dispatch_block_waves < 0 || t->dispatch_block_waves > moe::kMaxBlockWaves ||
+        t->combine_block_waves < 0 || t->combine_block_waves > moe::kMaxBlockWaves)
         return MOE_ERR_INVALID_ARG;
     if (t->dispatch_segments) ctx->tuning.dispatch_segments = t->dispatch_segments;
     if (t->combine_segments) ctx->tuning.combine_segments = t->combine_segments;
+    if (t->dispatch_block_waves) ctx->tuning.dispatch_block_waves = t->dispatch_block_waves;
+    if (t->combine_block_waves) ctx->tuning.combine_block_waves = t->combine_block_waves;
     ctx->tuning.dispatch_nontemporal = t->dispatch_nontemporal ? 1 : 0;
     ctx->tuning.combine_nontemporal = t->combine_nontemporal ? 1 : 0;
     return MOE_OK;
@@ -275,6 +285,7 @@ int moe_dispatch(moe_ctx* ctx, const void* d_x, const float* d_scores, const int
     a.x_e = at<void>(ctx, ctx->desc.x_e);
     a.s_e = at<float>(ctx, ctx->desc.s_e);
     a.segments = ctx->tuning.dispatch_segments;
+    a.block_waves = ctx->tuning.dispatch_block_waves;
     a.nontemporal = ctx->tuning.dispatch_nontemporal != 0;
     if (moe::launch_dispatch(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
@@ -302,6 +313,7 @@ int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
     a.bf16 = ctx->cfg.dtype == MOE_BF16;
     a.y = at<void>(ctx, ctx->desc.y);
     a.segments = ctx->tuning.combine_segments;
+    a.block_waves = ctx->tuning.combine_block_waves;
     a.nontemporal = ctx->tuning.combine_nontemporal != 0;
     if (moe::launch_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;

@@ -18,10 +18,11 @@ constexpr int kLayoutTile = kLayoutThreads * kLayoutSlotsPerLane;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
 
-// Dispatch and combine: workgroups of 4 wavefronts, one (token, segment)
-// work item per wavefront, 16-byte accesses per lane.
-constexpr int kMoveThreads = 256;
-constexpr int kMoveWaves = kMoveThreads / 64;
+// Dispatch and combine: one (token, row segment) work item per wavefront,
+// 16-byte accesses per lane, 1..16 wavefronts per workgroup (a launch-time
+// choice; kernels read it from blockDim).
+constexpr int kMaxBlockWaves = 16;
+constexpr int kMaxBlockThreads = kMaxBlockWaves * 64;
 constexpr int kMaxSegments = 16;
 
 static_assert(kMaxExperts % kLayoutThreads == 0, "experts split evenly over layout threads");
@@ -30,6 +31,10 @@ static_assert(kMaxExperts % kLayoutThreads == 0, "experts split evenly over layo
 inline int64_t layout_tiles(int64_t slots) {
     return (slots + kLayoutTile - 1) / kLayoutTile;
 }
+
+// Experts rounded up to a multiple of 4: the row stride of the per-tile
+// histograms, so rows can be read as 16-byte vectors.
+inline int32_t padded_experts(int32_t E) { return (E + 3) & ~3; }
 
 // Bits needed to tell experts 0..E-1 apart (0 for E == 1).
 inline int expert_bits(int32_t E) {
@@ -70,6 +75,7 @@ struct DispatchArgs {
     void* x_e;
     float* s_e;
     int32_t segments;
+    int32_t block_waves;    // wavefronts per workgroup, 1..16
     bool nontemporal;
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
@@ -85,6 +91,7 @@ struct CombineArgs {
     bool bf16;
     void* y;                // [T][row_bytes]
     int32_t segments;
+    int32_t block_waves;    // wavefronts per workgroup, 1..16
     bool nontemporal;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

@@ -187,10 +187,16 @@ class MoeDispatcher:
 
     # -- tuning ------------------------------------------------------------
     def set_tuning(self, dispatch_segments: int = 0, combine_segments: int = 0,
-                   dispatch_nontemporal: bool = False, combine_nontemporal: bool = False) -> None:
-        """Launch shape only; results never depend on it."""
-        t = L.MoeTuning(dispatch_segments, combine_segments, int(dispatch_nontemporal),
-                        int(combine_nontemporal))
+                   dispatch_nontemporal: Optional[bool] = None,
+                   combine_nontemporal: Optional[bool] = None,
+                   dispatch_block_waves: int = 0, combine_block_waves: int = 0) -> None:
+        """Launch shape only; results never depend on it. 0 / None keep the
+        current value."""
+        cur = self.get_tuning()
+        dnt = cur["dispatch_nontemporal"] if dispatch_nontemporal is None else dispatch_nontemporal
+        cnt = cur["combine_nontemporal"] if combine_nontemporal is None else combine_nontemporal
+        t = L.MoeTuning(dispatch_segments, combine_segments, int(dnt), int(cnt),
+                        dispatch_block_waves, combine_block_waves)
         L.check(self._lib.moe_set_tuning(self._ctx, C.byref(t)), "moe_set_tuning")
 
     def get_tuning(self) -> dict:
@@ -198,4 +204,6 @@ class MoeDispatcher:
         L.check(self._lib.moe_get_tuning(self._ctx, C.byref(t)), "moe_get_tuning")
         return {"dispatch_segments": t.dispatch_segments, "combine_segments": t.combine_segments,
                 "dispatch_nontemporal": bool(t.dispatch_nontemporal),
-                "combine_nontemporal": bool(t.combine_nontemporal)}
+                "combine_nontemporal": bool(t.combine_nontemporal),
+                "dispatch_block_waves": t.dispatch_block_waves,
+                "combine_block_waves": t.combine_block_waves}

@@ -92,7 +92,8 @@ typedef struct moe_config {
  *   s_e         f32   [nmax4*K]      score of each dispatched row; [0,total)
  *   x_e         dtype [nmax4*K][D]   expert-major hidden states; [0,total)
  *   y           dtype [nmax4][D]     combined output; rows [0,T) of a call
- *   block_hist  int32 [max_tiles][E] layout scratch (per-tile histograms)
+ *   block_hist  int32 [max_tiles][round_up4(E)] layout scratch (per-tile
+ *                                    histograms)
  * nmax4 = round_up4(num_max_tokens_per_rank). */
 typedef struct moe_buffers_desc {
     int64_t workspace_bytes;
@@ -181,15 +182,18 @@ int moe_combine(moe_ctx *ctx, const void *d_y_expert, const int32_t *d_row_map,
                 void *stream, void **d_y_out);
 
 /* Launch shape tuning (optional). Each token row is split into `segments`
- * wavefront work items (1..16); 0 keeps the current value. A nonzero
- * *_nontemporal marks dispatch's expert-buffer stores / combine's
- * expert-output loads as streaming (not kept in cache). Results do not depend
- * on any of these. Pure host. */
+ * wavefront work items (1..16) and `block_waves` wavefronts (1..16) form a
+ * workgroup; 0 keeps the current value. A nonzero *_nontemporal marks
+ * dispatch's expert-buffer stores / combine's expert-output loads as
+ * streaming (not kept in cache). Results do not depend on any of these.
+ * Pure host. */
 typedef struct moe_tuning {
     int32_t dispatch_segments;
     int32_t combine_segments;
     int32_t dispatch_nontemporal;
     int32_t combine_nontemporal;
+    int32_t dispatch_block_waves;
+    int32_t combine_block_waves;
 } moe_tuning;
 int moe_set_tuning(moe_ctx *ctx, const moe_tuning *tuning);
 int moe_get_tuning(const moe_ctx *ctx, moe_tuning *out);

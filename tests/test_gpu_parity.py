@@ -232,7 +232,8 @@ def _edge(T, ntpr, nmax, D, E, K, dtype, ids, scores=None, seed=0, segments=None
     if segments:
         disp.set_tuning(dispatch_segments=segments[0], combine_segments=segments[1],
                         dispatch_nontemporal=bool(segments[2]),
-                        combine_nontemporal=bool(segments[2]))
+                        combine_nontemporal=bool(segments[2]),
+                        dispatch_block_waves=segments[3], combine_block_waves=segments[4])
     note(f"edge T={T} ntpr={ntpr} nmax={nmax} D={D} E={E} K={K} {dtype} seg={segments}")
     g = run_gpu(disp, x, ids, scores, T, ntpr)
     o = oracle.run_pipeline(x, ids, scores, T, ntpr, E, K)
@@ -285,7 +286,8 @@ def test_single_expert_single_slot_smallest_row():
     _edge(5, 7, 9, 4, 1, 1, "f32", ids)
 
 
-@pytest.mark.parametrize("segments", [(1, 1, 0), (2, 3, 1), (16, 16, 0), (5, 2, 1)])
+@pytest.mark.parametrize("segments", [(1, 1, 0, 1, 1), (2, 3, 1, 16, 3), (16, 16, 0, 7, 16),
+                                      (5, 2, 1, 4, 4), (14, 14, 0, 14, 4)])
 def test_ragged_row_and_launch_shapes(segments):
     rng = np.random.default_rng(5)
     T, E, K = 1001, 64, 8

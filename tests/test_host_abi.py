@@ -99,7 +99,7 @@ def test_workspace_carve_up(lib, nmax, D, E, K, dtype):
     assert d.nmax4 == n4 and d.max_rows == n4 * K and d.row_bytes == D * eb
     sizes = {"counts": E * 4, "offsets": (E + 1) * 4, "row_map": n4 * K * 4,
              "src_map": n4 * K * 4, "s_e": n4 * K * 4, "x_e": n4 * K * D * eb,
-             "y": n4 * D * eb, "block_hist": d.max_tiles * E * 4}
+             "y": n4 * D * eb, "block_hist": d.max_tiles * oracle.round_up4(E) * 4}
     assert d.max_tiles * d.tile_slots >= n4 * K
     spans = sorted((getattr(d, k), getattr(d, k) + v, k) for k, v in sizes.items())
     for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
@@ -163,16 +163,19 @@ def test_tuning_roundtrip_and_limits(lib):
     t = L.MoeTuning()
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
     assert 1 <= t.dispatch_segments <= 16 and 1 <= t.combine_segments <= 16
-    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1))) == L.MOE_OK
+    assert 1 <= t.dispatch_block_waves <= 16 and 1 <= t.combine_block_waves <= 16
+    # 7168 bf16 = 896 chunks: 14 one-chunk segments; a dispatch workgroup per token row
+    assert (t.dispatch_segments, t.dispatch_block_waves, t.combine_block_waves) == (14, 14, 4)
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16))) == L.MOE_OK
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
     assert (t.dispatch_segments, t.combine_segments, t.dispatch_nontemporal,
-            t.combine_nontemporal) == (4, 3, 1, 1)
-    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(0, 0, 0, 0))) == L.MOE_OK
+            t.combine_nontemporal, t.dispatch_block_waves, t.combine_block_waves) == (4, 3, 1, 1, 2, 16)
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(0, 0, 0, 0, 0, 0))) == L.MOE_OK
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
     assert (t.dispatch_segments, t.combine_segments, t.dispatch_nontemporal,
-            t.combine_nontemporal) == (4, 3, 0, 0)
-    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(17, 1, 0, 0))) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(-1, 1, 0, 0))) == L.MOE_ERR_INVALID_ARG
+            t.combine_nontemporal, t.dispatch_block_waves, t.combine_block_waves) == (4, 3, 0, 0, 2, 16)
+    for bad in ((17, 1, 0, 0, 0, 0), (-1, 1, 0, 0, 0, 0), (1, 1, 0, 0, 17, 0), (1, 1, 0, 0, 0, -2)):
+        assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(*bad))) == L.MOE_ERR_INVALID_ARG
     lib.moe_destroy(ctx)
 
 
