@@ -23,7 +23,8 @@
 // double-buffered: the next chunk's K loads are issued before the current
 // chunk is reduced and stored. No-expert slots load the token's first valid
 // row instead (always written, finite) and skip it in the sum, which keeps
-// every load unconditional.
+// every load unconditional. Output stores are ordinary, or streaming when the
+// output buffer is larger than the last-level cache (single-chunk shape).
 #include "moe_kernels.h"
 
 namespace moe {
@@ -92,7 +93,9 @@ __device__ __forceinline__ v4i fetch(const v4i* p) {
 // One wavefront per (token, row segment). SINGLE: the segment is exactly one
 // 16-byte chunk per lane, so no loop and no second buffer (fewer registers,
 // more wavefronts resident); otherwise the segment is walked chunk by chunk.
-template <int K, bool BF16, bool NT, bool SINGLE>
+// NT: streaming loads of the expert outputs. NTS (SINGLE only): streaming
+// stores of y.
+template <int K, bool BF16, bool NT, bool SINGLE, bool NTS>
 __global__ __launch_bounds__(kMaxBlockThreads)
 void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row_map,
                     const float* __restrict__ scores, int32_t T, int32_t chunks,
@@ -174,7 +177,12 @@ void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row
 #pragma unroll
         for (int k = 0; k < K; ++k) b[k] = fetch<NT>(src[k] + cl);
         const v4i out = all_valid ? reduce(b, true) : reduce(b, false);
-        if (c < c_end) dst[c] = out;
+        if (c < c_end) {
+            if constexpr (NTS)
+                __builtin_nontemporal_store(out, dst + c);
+            else
+                dst[c] = out;
+        }
         return;
     } else {
         const int32_t iters = (c_end - c_begin + 63) / 64;   // one chunk per lane each
@@ -217,10 +225,14 @@ hipError_t launch_k(const CombineArgs& a, int32_t segments, int32_t seg_chunks,
     const int64_t items = int64_t(a.T) * segments;
     const int64_t blocks = (items + a.block_waves - 1) / a.block_waves;
     const bool single = seg_chunks == 64;
-    auto kernel = a.nontemporal ? (single ? combine_kernel<K, BF16, true, true>
-                                          : combine_kernel<K, BF16, true, false>)
-                                : (single ? combine_kernel<K, BF16, false, true>
-                                          : combine_kernel<K, BF16, false, false>);
+    const bool nts = a.store_nontemporal;
+    auto kernel = a.nontemporal
+        ? (single ? (nts ? combine_kernel<K, BF16, true, true, true>
+                         : combine_kernel<K, BF16, true, true, false>)
+                  : combine_kernel<K, BF16, true, false, false>)
+        : (single ? (nts ? combine_kernel<K, BF16, false, true, true>
+                         : combine_kernel<K, BF16, false, true, false>)
+                  : combine_kernel<K, BF16, false, false, false>);
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * a.block_waves), 0, stream,
                        static_cast<const v4i*>(a.y_e), a.row_map, a.scores, a.T, a.chunks,
                        segments, seg_chunks, a.row_limit, static_cast<v4i*>(a.y));

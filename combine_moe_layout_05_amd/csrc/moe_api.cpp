@@ -201,6 +201,10 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     c->tuning.combine_nontemporal = 1;
     c->tuning.dispatch_block_waves = seg_eff >= 4 ? seg_eff : moe::kMaxBlockWaves;
     c->tuning.combine_block_waves = 4;
+    // Stream y past the caches when the whole output buffer exceeds the
+    // last-level cache: it cannot stay cached for its consumer, and ordinary
+    // stores would leave dirty lines to be written back during later kernels.
+    c->tuning.combine_store_nontemporal = d.nmax4 * d.row_bytes > moe::kLastLevelCacheBytes ? 1 : 0;
     *out = c;
     return MOE_OK;
 }
@@ -227,6 +231,8 @@ int moe_set_tuning(moe_ctx* ctx, const moe_tuning* t) {
     if (t->combine_segments) ctx->tuning.combine_segments = t->combine_segments;
     if (t->dispatch_block_waves) ctx->tuning.dispatch_block_waves = t->dispatch_block_waves;
     if (t->combine_block_waves) ctx->tuning.combine_block_waves = t->combine_block_waves;
+    if (t->combine_store_nontemporal >= 0)
+        ctx->tuning.combine_store_nontemporal = t->combine_store_nontemporal ? 1 : 0;
     ctx->tuning.dispatch_nontemporal = t->dispatch_nontemporal ? 1 : 0;
     ctx->tuning.combine_nontemporal = t->combine_nontemporal ? 1 : 0;
     return MOE_OK;
@@ -315,6 +321,7 @@ int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
     a.segments = ctx->tuning.combine_segments;
     a.block_waves = ctx->tuning.combine_block_waves;
     a.nontemporal = ctx->tuning.combine_nontemporal != 0;
+    a.store_nontemporal = ctx->tuning.combine_store_nontemporal != 0;
     if (moe::launch_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     *d_y_out = a.y;

@@ -24,6 +24,9 @@ constexpr int kMaxTopk = 16;
 constexpr int kMaxBlockWaves = 16;
 constexpr int kMaxBlockThreads = kMaxBlockWaves * 64;
 constexpr int kMaxSegments = 16;
+// MI355X last-level (Infinity) cache: outputs larger than this cannot stay
+// cached for their consumer anyway.
+constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;
 
 static_assert(kMaxExperts % kLayoutThreads == 0, "experts split evenly over layout threads");
 
@@ -92,7 +95,8 @@ struct CombineArgs {
     void* y;                // [T][row_bytes]
     int32_t segments;
     int32_t block_waves;    // wavefronts per workgroup, 1..16
-    bool nontemporal;
+    bool nontemporal;       // streaming loads of the expert outputs
+    bool store_nontemporal; // streaming stores of y
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

@@ -189,14 +189,16 @@ class MoeDispatcher:
     def set_tuning(self, dispatch_segments: int = 0, combine_segments: int = 0,
                    dispatch_nontemporal: Optional[bool] = None,
                    combine_nontemporal: Optional[bool] = None,
-                   dispatch_block_waves: int = 0, combine_block_waves: int = 0) -> None:
+                   dispatch_block_waves: int = 0, combine_block_waves: int = 0,
+                   combine_store_nontemporal: Optional[bool] = None) -> None:
         """Launch shape only; results never depend on it. 0 / None keep the
         current value."""
         cur = self.get_tuning()
         dnt = cur["dispatch_nontemporal"] if dispatch_nontemporal is None else dispatch_nontemporal
         cnt = cur["combine_nontemporal"] if combine_nontemporal is None else combine_nontemporal
+        snt = -1 if combine_store_nontemporal is None else int(combine_store_nontemporal)
         t = L.MoeTuning(dispatch_segments, combine_segments, int(dnt), int(cnt),
-                        dispatch_block_waves, combine_block_waves)
+                        dispatch_block_waves, combine_block_waves, snt)
         L.check(self._lib.moe_set_tuning(self._ctx, C.byref(t)), "moe_set_tuning")
 
     def get_tuning(self) -> dict:
@@ -206,4 +208,5 @@ class MoeDispatcher:
                 "dispatch_nontemporal": bool(t.dispatch_nontemporal),
                 "combine_nontemporal": bool(t.combine_nontemporal),
                 "dispatch_block_waves": t.dispatch_block_waves,
-                "combine_block_waves": t.combine_block_waves}
+                "combine_block_waves": t.combine_block_waves,
+                "combine_store_nontemporal": bool(t.combine_store_nontemporal)}

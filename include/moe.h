@@ -184,9 +184,9 @@ int moe_combine(moe_ctx *ctx, const void *d_y_expert, const int32_t *d_row_map,
 /* Launch shape tuning (optional). Each token row is split into `segments`
  * wavefront work items (1..16) and `block_waves` wavefronts (1..16) form a
  * workgroup; 0 keeps the current value. A nonzero *_nontemporal marks
- * dispatch's expert-buffer stores / combine's expert-output loads as
- * streaming (not kept in cache). Results do not depend on any of these.
- * Pure host. */
+ * dispatch's expert-buffer stores / combine's expert-output loads / combine's
+ * output stores as streaming (not kept in cache); for the last one -1 keeps
+ * the current value. Results do not depend on any of these. Pure host. */
 typedef struct moe_tuning {
     int32_t dispatch_segments;
     int32_t combine_segments;
@@ -194,6 +194,7 @@ typedef struct moe_tuning {
     int32_t combine_nontemporal;
     int32_t dispatch_block_waves;
     int32_t combine_block_waves;
+    int32_t combine_store_nontemporal;  /* streaming stores of y; -1 keeps */
 } moe_tuning;
 int moe_set_tuning(moe_ctx *ctx, const moe_tuning *tuning);
 int moe_get_tuning(const moe_ctx *ctx, moe_tuning *out);

@@ -233,7 +233,8 @@ def _edge(T, ntpr, nmax, D, E, K, dtype, ids, scores=None, seed=0, segments=None
         disp.set_tuning(dispatch_segments=segments[0], combine_segments=segments[1],
                         dispatch_nontemporal=bool(segments[2]),
                         combine_nontemporal=bool(segments[2]),
-                        dispatch_block_waves=segments[3], combine_block_waves=segments[4])
+                        dispatch_block_waves=segments[3], combine_block_waves=segments[4],
+                        combine_store_nontemporal=bool(segments[2]))
     note(f"edge T={T} ntpr={ntpr} nmax={nmax} D={D} E={E} K={K} {dtype} seg={segments}")
     g = run_gpu(disp, x, ids, scores, T, ntpr)
     o = oracle.run_pipeline(x, ids, scores, T, ntpr, E, K)
