@@ -270,3 +270,74 @@ void orc_combine_tokens(const void *y_e, int dtype, int64_t D,
         orc_combine_token(y_e, dtype, D, row_map, scores, K, tokens[j],
                           (uint8_t *)out + j * D * elem);
 }
+
+/* ---------------------------------------------------------------------- */
+/* Backward ([NA] "Testing": the unequal-count run must reproduce the
+ * equal-count run bitwise in forward and backward). The derivatives of the
+ * forward definitions above:
+ *   combine: y[t] = sum_k s[t][k] * y_e[r(t,k)]
+ *     dL/dy_e[r(t,k)] = s[t][k] * dL/dy[t]
+ *     dL/ds[t][k]     = <dL/dy[t], y_e[r(t,k)]>        (0 for no expert)
+ *   dispatch: x_e[r(t,k)] = x[t]
+ *     dL/dx[t] = sum_k dL/dx_e[r(t,k)]                  (+0.0 if none)
+ * Precision: the scaled copy is one fp32 product rounded to the element
+ * dtype; the gather-sum is fp32, slots in ascending k, from +0.0; the dot
+ * product is the exact value computed in fp64 (its fp32 evaluation order
+ * on the GPU is not fixed by the definition).                          */
+
+static void orc_store_elem(void *buf, int dtype, int64_t idx, float v)
+{
+    if (dtype == 0)
+        ((float *)buf)[idx] = v;
+    else
+        ((uint16_t *)buf)[idx] = orc_f32_to_bf16(v);
+}
+
+/* g [T][D], y_e [rows][D] (element dtype), row_map [T][K], scores [T][K].
+ * Writes g_e rows r(t,k) (other rows untouched) and grad_s [T][K] (fp64). */
+void orc_combine_backward(const void *g, const void *y_e, int dtype, int64_t D,
+                          const int32_t *row_map, const float *scores,
+                          int64_t T, int32_t K, void *g_e, double *grad_s,
+                          int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t r = row_map[t * K + k];
+            if (r < 0) {
+                grad_s[t * K + k] = 0.0;
+                continue;
+            }
+            float s = scores[t * K + k];
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                float gv = orc_load_elem(g, dtype, t * D + d);
+                float yv = orc_load_elem(y_e, dtype, (int64_t)r * D + d);
+                dot += (double)gv * (double)yv;
+                orc_store_elem(g_e, dtype, (int64_t)r * D + d, s * gv);
+            }
+            grad_s[t * K + k] = dot;
+        }
+    }
+}
+
+/* h [rows][D] (element dtype), row_map [T][K]: gx [T][D]. */
+void orc_dispatch_backward(const void *h, int dtype, int64_t D,
+                           const int32_t *row_map, int64_t T, int32_t K,
+                           void *gx, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t d = 0; d < D; ++d) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int32_t r = row_map[t * K + k];
+                if (r < 0) continue;
+                acc = acc + orc_load_elem(h, dtype, (int64_t)r * D + d);
+            }
+            orc_store_elem(gx, dtype, t * D + d, acc);
+        }
+    }
+}

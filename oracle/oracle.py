@@ -62,6 +62,10 @@ def _load():
         L.orc_combine.argtypes = [vp, C.c_int, i64, vp, vp, i64, i32, vp, C.c_int]; L.orc_combine.restype = None
         L.orc_combine_tokens.argtypes = [vp, C.c_int, i64, vp, vp, i32, vp, i64, vp]; L.orc_combine_tokens.restype = None
         L.orc_f32_to_bf16.argtypes = [C.c_float]; L.orc_f32_to_bf16.restype = C.c_uint16
+        L.orc_combine_backward.argtypes = [vp, vp, C.c_int, i64, vp, vp, i64, i32, vp, vp, C.c_int]
+        L.orc_combine_backward.restype = None
+        L.orc_dispatch_backward.argtypes = [vp, C.c_int, i64, vp, i64, i32, vp, C.c_int]
+        L.orc_dispatch_backward.restype = None
         _lib = L
         return L
 
@@ -207,3 +211,38 @@ def run_pipeline(x: np.ndarray, ids: np.ndarray, scores: np.ndarray, T: int,
     y = combine(x_e, lay["row_map"], scores[:T], T, K, nthreads)
     lay.update(x_e=x_e, s_e=s_e, y=y)
     return lay
+
+
+def combine_backward(g: np.ndarray, y_e: np.ndarray, row_map: np.ndarray,
+                     scores: np.ndarray, T: int, K: int, nthreads: int = 1):
+    """(g_e [rows, D] with rows r(t,k) written and the rest zero,
+    grad_s [T, K] float64) for dL/dy = g [T, D]."""
+    L = _load()
+    g = np.ascontiguousarray(g)
+    y_e = np.ascontiguousarray(y_e)
+    if g.dtype != y_e.dtype:
+        raise TypeError("g and y_e need the same element dtype")
+    row_map = np.ascontiguousarray(row_map, dtype=np.int32)
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    D = y_e.shape[1]
+    g_e = np.zeros_like(y_e)
+    grad_s = np.zeros((T, K), np.float64)
+    if T:
+        L.orc_combine_backward(_ptr(g), _ptr(y_e), _dtype_code(y_e), D, _ptr(row_map),
+                               _ptr(scores), T, K, _ptr(g_e), _ptr(grad_s), nthreads)
+    return g_e, grad_s
+
+
+def dispatch_backward(h: np.ndarray, row_map: np.ndarray, T: int, K: int,
+                      nthreads: int = 1) -> np.ndarray:
+    """gx [T, D] = sum over each token's slots of h rows (fp32, k order)."""
+    L = _load()
+    h = np.ascontiguousarray(h)
+    row_map = np.ascontiguousarray(row_map, dtype=np.int32)
+    D = h.shape[1]
+    gx = np.empty((T, D), h.dtype)
+    if T:
+        h_arg = h if h.size else np.zeros((1, D), h.dtype)
+        L.orc_dispatch_backward(_ptr(h_arg), _dtype_code(h), D, _ptr(row_map), T, K,
+                                _ptr(gx), nthreads)
+    return gx

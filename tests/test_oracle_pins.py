@@ -481,3 +481,141 @@ def test_virtual_padding_equals_materialized_padding():
             assert np.array_equal(virt[key], mat[key]), key
         assert np.array_equal(virt["y"], mat["y"][:T])
         assert (mat["y"][T:] == 0).all()  # padded rows are +0.0, then sliced off
+
+
+# --------------------------------------------------------------------------
+# Backward: pinned by the adjoint identities and by finite differences of the
+# forward definitions, with inputs chosen so that every fp32/bf16 operation
+# is exact (small integers, dyadic scores): then the identities hold exactly.
+
+def _exact_case(T, E, K, dtype, seed, none_frac=0.15):
+    rng = np.random.default_rng(seed)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    ids[rng.random((T, K)) < none_frac] = -1
+    scores = rng.choice(np.array([0.5, 0.25, 0.125, 0.0625, -0.5, 1.0], np.float32), size=(T, K))
+    lay = oracle.layout(ids, T, T, E, K)
+    def ints(shape):
+        v = rng.integers(-8, 9, size=shape).astype(np.float32)
+        return v if dtype == "f32" else _torch_bf16_bits(v)
+    return ids, scores, lay, ints
+
+
+def _f64(a):
+    return a.astype(np.float64) if a.dtype == np.float32 else _bf16_to_f64(a)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dispatch_backward_is_the_adjoint_of_dispatch(dtype):
+    T, E, K, D = 37, 12, 4, 24
+    ids, scores, lay, ints = _exact_case(T, E, K, dtype, 21)
+    x = ints((T, D))
+    x_e, _ = oracle.dispatch(x, scores, K, lay["src"])
+    h = ints((lay["total"], D))
+    gx = oracle.dispatch_backward(h, lay["row_map"], T, K)
+    lhs = float(np.sum(_f64(x_e) * _f64(h)))       # <dispatch(x), h>
+    rhs = float(np.sum(_f64(x) * _f64(gx)))        # <x, dispatch^T h>
+    assert lhs == rhs
+    # brute force: gx[t] = sum over the token's slots of h rows
+    want = np.zeros((T, D))
+    for t in range(T):
+        for k in range(K):
+            r = lay["row_map"][t, k]
+            if r >= 0:
+                want[t] += _f64(h[r:r + 1])[0]
+    assert np.array_equal(_f64(gx), want)
+
+
+def test_dispatch_backward_equals_unit_score_combine():
+    w = workloads.WORKLOADS["padded"]
+    b = workloads.make_batch(w)
+    T = 300
+    lay = oracle.layout(b["ids"][:T], T, T, w.E, w.K)
+    rng = np.random.default_rng(3)
+    h = _torch_bf16_bits(rng.standard_normal((lay["total"], 40)).astype(np.float32))
+    gx = oracle.dispatch_backward(h, lay["row_map"], T, w.K)
+    ones = np.ones((T, w.K), np.float32)
+    assert np.array_equal(gx, oracle.combine(h, lay["row_map"], ones, T, w.K))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_backward_is_the_adjoint_in_expert_outputs(dtype):
+    T, E, K, D = 41, 10, 4, 20
+    ids, scores, lay, ints = _exact_case(T, E, K, dtype, 22)
+    y_e = ints((lay["total"], D))
+    g = ints((T, D))
+    y = oracle.combine(y_e, lay["row_map"], scores, T, K)
+    g_e, grad_s = oracle.combine_backward(g, y_e, lay["row_map"], scores, T, K)
+    lhs = float(np.sum(_f64(y) * _f64(g)))          # <combine(y_e), g>
+    rhs = float(np.sum(_f64(y_e) * _f64(g_e)))      # <y_e, combine^T g>
+    assert lhs == rhs
+    # brute force of both outputs
+    for t in range(T):
+        for k in range(K):
+            r = lay["row_map"][t, k]
+            if r < 0:
+                assert grad_s[t, k] == 0.0
+                continue
+            assert np.array_equal(_f64(g_e[r:r + 1])[0], float(scores[t, k]) * _f64(g[t:t + 1])[0])
+            assert grad_s[t, k] == float(np.dot(_f64(g[t:t + 1])[0], _f64(y_e[r:r + 1])[0]))
+
+
+def test_combine_backward_score_gradient_by_finite_differences():
+    # L(s) = sum_t <g[t], y[t]> is linear in s, so (L(s + d e_tk) - L(s)) / d
+    # is exactly dL/ds[t,k]; every forward operation is exact here.
+    T, E, K, D = 9, 8, 4, 16
+    ids, scores, lay, ints = _exact_case(T, E, K, "f32", 23, none_frac=0.2)
+    y_e = ints((lay["total"], D))
+    g = ints((T, D))
+    _, grad_s = oracle.combine_backward(g, y_e, lay["row_map"], scores, T, K)
+    base = float(np.sum(oracle.combine(y_e, lay["row_map"], scores, T, K).astype(np.float64) * g))
+    delta = np.float32(1.0 / 32)
+    for t in range(T):
+        for k in range(K):
+            s2 = scores.copy()
+            s2[t, k] += delta
+            Lp = float(np.sum(oracle.combine(y_e, lay["row_map"], s2, T, K).astype(np.float64) * g))
+            fd = (Lp - base) / float(delta)
+            assert fd == grad_s[t, k], (t, k)
+
+
+def test_combine_backward_general_values_within_bounds():
+    rng = np.random.default_rng(24)
+    T, E, K, D = 120, 32, 8, 64
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    ids[rng.random((T, K)) < 0.1] = -1
+    scores = rng.standard_normal((T, K)).astype(np.float32)
+    lay = oracle.layout(ids, T, T, E, K)
+    y_e = _torch_bf16_bits(rng.standard_normal((lay["total"], D)).astype(np.float32))
+    g = _torch_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+    g_e, grad_s = oracle.combine_backward(g, y_e, lay["row_map"], scores, T, K)
+    G, Y = _f64(g), _f64(y_e)
+    for t in range(T):
+        for k in range(K):
+            r = lay["row_map"][t, k]
+            if r < 0:
+                continue
+            exact = scores[t, k] * G[t]
+            got = _f64(g_e[r:r + 1])[0]
+            # one fp32 product, then one bf16 rounding
+            assert np.all(np.abs(got - exact) <= np.abs(exact) * (2.0 ** -8 + 2.0 ** -24) + 2.0 ** -133)
+            assert abs(grad_s[t, k] - np.dot(G[t], Y[r])) <= 1e-12 * np.sum(np.abs(G[t] * Y[r]))
+
+
+def test_backward_unequal_counts_reproduce_equal_count_run():
+    w, b = _small_padded_batch()
+    rng = np.random.default_rng(25)
+    D = w.D
+    g_full = _torch_bf16_bits(rng.standard_normal((2048, D)).astype(np.float32))
+    lay_f = oracle.layout(b["ids"], 2048, 2048, w.E, w.K)
+    x_e_f, _ = oracle.dispatch(b["x"], b["scores"], w.K, lay_f["src"])
+    ge_f, gs_f = oracle.combine_backward(g_full, x_e_f, lay_f["row_map"], b["scores"], 2048, w.K)
+    gx_f = oracle.dispatch_backward(ge_f, lay_f["row_map"], 2048, w.K)
+    for T in workloads.PADDED_T_VALUES:
+        lay = oracle.layout(b["ids"][:T], T, 2048, w.E, w.K)
+        x_e, _ = oracle.dispatch(b["x"][:T], b["scores"][:T], w.K, lay["src"])
+        ge, gs = oracle.combine_backward(g_full[:T], x_e, lay["row_map"], b["scores"][:T], T, w.K)
+        gx = oracle.dispatch_backward(ge, lay["row_map"], T, w.K)
+        assert np.array_equal(gs, gs_f[:T])
+        assert np.array_equal(gx, gx_f[:T])
+        rm, rmf = lay["row_map"][:T].ravel(), lay_f["row_map"][:T].ravel()
+        assert np.array_equal(ge[rm[rm >= 0]], ge_f[rmf[rmf >= 0]])   # per slot
