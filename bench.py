@@ -26,7 +26,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "combine_moe_layout_05_amd", "csrc")
 KERNEL_SOURCES = {
     "dispatch": ["dispatch.hip", "moe_kernels.h"],
-    "combine": ["combine.hip", "moe_kernels.h"],
+    "combine": ["combine.hip", "moe_lanes.h", "moe_kernels.h"],
     "layout": ["layout.hip", "moe_kernels.h"],
 }
 METRIC = ("dispatch+combine tokens/s and achieved HBM GB/s (% of peak), "

@@ -19,6 +19,9 @@ MOE_ERR_CAPACITY = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_ERR_STATE = -5
+MOE_ERR_UNSUPPORTED = -6
+
+MOE_FLAG_BACKWARD = 1
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -33,14 +36,14 @@ _i32, _i64, _vp, _int = C.c_int32, C.c_int64, C.c_void_p, C.c_int
 
 class MoeConfig(C.Structure):
     _fields_ = [("num_max_tokens_per_rank", _i32), ("hidden", _i32),
-                ("num_experts", _i32), ("topk", _i32), ("dtype", _i32)]
+                ("num_experts", _i32), ("topk", _i32), ("dtype", _i32), ("flags", _i32)]
 
 
 class MoeBuffersDesc(C.Structure):
     _fields_ = [(n, _i64) for n in (
         "workspace_bytes", "nmax4", "max_rows", "row_bytes", "max_tiles", "tile_slots",
         "counts", "offsets", "row_map", "src_map", "s_e", "x_e", "y",
-        "block_hist")]
+        "block_hist", "g_e", "g_s", "g_x")]
 
 
 class MoeTuning(C.Structure):
@@ -58,6 +61,9 @@ SIGNATURES = {
     "moe_layout": (_int, [_vp, _vp, _i32, _i32, _vp]),
     "moe_dispatch": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "moe_combine": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
+    "moe_combine_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp),
+                                    C.POINTER(_vp)]),
+    "moe_dispatch_backward": (_int, [_vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
     "moe_set_tuning": (_int, [_vp, C.POINTER(MoeTuning)]),
     "moe_get_tuning": (_int, [_vp, C.POINTER(MoeTuning)]),
     "moe_ceil_div": (_i64, [_i64, _i64]),

@@ -19,8 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "moe_api.cpp"]
-HEADERS = [os.path.join(CSRC, "moe_kernels.h"), os.path.join(INCLUDE, "moe.h")]
+SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "combine_backward.hip", "moe_api.cpp"]
+HEADERS = [os.path.join(CSRC, "moe_kernels.h"), os.path.join(CSRC, "moe_lanes.h"),
+           os.path.join(INCLUDE, "moe.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -6,6 +6,8 @@
 // token-ordered output and slices the padding off; with identity experts a
 // token's output depends only on its own routing):
 //   y[t] = sum_{k=0..K-1, row_map[t][k] >= 0} scores[t][k] * y_e[row_map[t][k]]
+// (with scores == nullptr every weight is 1: the gather-sum that is the
+// backward of dispatch, dL/dx[t] = sum_k dL/dx_e[row_map[t][k]])
 // in fp32, fused multiply-add in ascending k, starting from +0.0, stored in
 // the element type (bf16 rounds to nearest even; NaN becomes 0x7FC0). A slot
 // without an expert is skipped and its score is not read. Only t < T is
@@ -26,69 +28,10 @@
 // every load unconditional. Output stores are ordinary, or streaming when the
 // output buffer is larger than the last-level cache (single-chunk shape).
 #include "moe_kernels.h"
+#include "moe_lanes.h"
 
 namespace moe {
 namespace {
-
-typedef int32_t v4i __attribute__((ext_vector_type(4)));
-
-// bf16 <-> fp32 by bit manipulation: widening is exact; narrowing rounds to
-// nearest even, with every NaN mapped to the quiet NaN 0x7FC0.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-template <bool BF16>
-struct Lanes;
-
-template <>
-struct Lanes<false> {  // 4 fp32 per 16-byte chunk
-    static constexpr int N = 4;
-    __device__ static void fma_into(float (&acc)[N], float s, v4i v) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] = __builtin_fmaf(s, __int_as_float(v[i]), acc[i]);
-    }
-    __device__ static v4i pack(const float (&acc)[N]) {
-        v4i o;
-#pragma unroll
-        for (int i = 0; i < N; ++i) o[i] = __float_as_int(acc[i]);
-        return o;
-    }
-};
-
-template <>
-struct Lanes<true> {  // 8 bf16 per 16-byte chunk, element 2i in the low half
-    static constexpr int N = 8;
-    __device__ static void fma_into(float (&acc)[N], float s, v4i v) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w = static_cast<uint32_t>(v[i]);
-            acc[2 * i] = __builtin_fmaf(s, bf16_lo(w), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(s, bf16_hi(w), acc[2 * i + 1]);
-        }
-    }
-    __device__ static v4i pack(const float (&acc)[N]) {
-        v4i o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[i] = static_cast<int32_t>(f32_to_bf16_bits(acc[2 * i]) |
-                                        (f32_to_bf16_bits(acc[2 * i + 1]) << 16));
-        return o;
-    }
-};
-
-template <bool NT>
-__device__ __forceinline__ v4i fetch(const v4i* p) {
-    if constexpr (NT)
-        return __builtin_nontemporal_load(p);
-    else
-        return *p;
-}
 
 // One wavefront per (token, row segment). SINGLE: the segment is exactly one
 // 16-byte chunk per lane, so no loop and no second buffer (fewer registers,
@@ -120,7 +63,7 @@ void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row
         const int32_t r = row_map[t_first * K + tid];
         const bool ok = r >= 0 && r < row_limit;
         tile_rows[tid] = ok ? r : -1;
-        tile_scores[tid] = ok ? scores[t_first * K + tid] : 0.0f;
+        tile_scores[tid] = ok ? (scores ? scores[t_first * K + tid] : 1.0f) : 0.0f;
     }
     __syncthreads();
 

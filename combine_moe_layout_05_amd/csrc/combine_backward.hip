@@ -1,0 +1,125 @@
+// Backward of the combine on gfx950.
+//
+// What is computed (the derivatives of the combine y[t] = sum_k s[t][k] *
+// y_e[r(t,k)]; "fix(moe): equalize and align per-rank token counts for
+// HybridEP dispatch", section "Testing", checks forward and backward of the
+// dispatcher bitwise against the equal-count run):
+//   dL/dy_e[r(t,k)] = s[t][k] * dL/dy[t]      one fp32 product, rounded to
+//                                             the element type
+//   dL/ds[t][k]     = <dL/dy[t], y_e[r(t,k)]> fp32 fused multiply-adds
+// for every slot with an expert; a no-expert slot gets dL/ds = +0.0 and no
+// row. Rows of dL/dy_e past the true total are not written.
+//
+// One workgroup per token, W = ceil(chunks/64) wavefronts (at most 16): each
+// lane owns 16-byte chunks lane + 64*wave + 64*W*i of the row, so the
+// workgroup reads dL/dy[t] once, reads the K expert rows (streaming loads),
+// writes the K scaled rows, and reduces the K dot products: in element order
+// within a lane, then a fixed butterfly over the 64 lanes, then the
+// wavefronts in order. The reduction order is fixed, so results are
+// deterministic; it differs from plain left-to-right order, which stays
+// within the fp32 summation error bound of the dot product.
+#include "moe_kernels.h"
+#include "moe_lanes.h"
+
+namespace moe {
+namespace {
+
+template <int K, bool BF16>
+__global__ __launch_bounds__(kMaxBlockThreads)
+void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restrict__ y_e,
+                             const int32_t* __restrict__ row_map,
+                             const float* __restrict__ scores, int32_t chunks,
+                             int64_t row_limit, v4i* __restrict__ grad_y_e,
+                             float* __restrict__ grad_s) {
+    using L = Lanes<BF16>;
+    __shared__ int32_t tok_rows[K];
+    __shared__ float tok_scores[K];
+    __shared__ float partial[kMaxBlockWaves][K];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int waves = static_cast<int>(blockDim.x) >> 6;
+    const int64_t t = blockIdx.x;
+
+    if (tid < K) {
+        const int32_t r = row_map[t * K + tid];
+        const bool ok = r >= 0 && r < row_limit;
+        tok_rows[tid] = ok ? r : -1;
+        tok_scores[tid] = ok ? scores[t * K + tid] : 0.0f;
+    }
+    __syncthreads();
+    int32_t row[K];
+    float s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        row[k] = __builtin_amdgcn_readfirstlane(tok_rows[k]);
+        s[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tok_scores[k])));
+    }
+
+    float dot[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) dot[k] = 0.0f;
+    const v4i* g = grad_y + t * chunks;
+    for (int32_t c = wave * 64 + lane; c < chunks; c += waves * 64) {
+        const v4i gv = g[c];
+        v4i yv[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (row[k] >= 0) yv[k] = fetch<true>(y_e + int64_t(row[k]) * chunks + c);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (row[k] < 0) continue;
+            grad_y_e[int64_t(row[k]) * chunks + c] = L::scale(s[k], gv);
+            dot[k] = L::dot_into(dot[k], gv, yv[k]);
+        }
+    }
+
+    // Lanes, then wavefronts, in a fixed order.
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float v = dot[k];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) partial[wave][k] = v;
+    }
+    __syncthreads();
+    if (tid < K) {
+        float sum = 0.0f;
+        for (int w = 0; w < waves; ++w) sum += partial[w][tid];
+        grad_s[t * K + tid] = tok_rows[tid] >= 0 ? sum : 0.0f;
+    }
+}
+
+template <int K, bool BF16>
+hipError_t launch_k(const CombineBackwardArgs& a, hipStream_t stream) {
+    int32_t waves = (a.chunks + 63) / 64;
+    if (waves > kMaxBlockWaves) waves = kMaxBlockWaves;
+    hipLaunchKernelGGL((combine_backward_kernel<K, BF16>), dim3(static_cast<uint32_t>(a.T)),
+                       dim3(64 * waves), 0, stream, static_cast<const v4i*>(a.grad_y),
+                       static_cast<const v4i*>(a.y_e), a.row_map, a.scores, a.chunks,
+                       a.row_limit, static_cast<v4i*>(a.grad_y_e), a.grad_s);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_dtype(const CombineBackwardArgs& a, hipStream_t stream) {
+    switch (a.K) {
+#define MOE_CB_CASE(k) \
+    case k: return launch_k<k, BF16>(a, stream);
+        MOE_CB_CASE(1) MOE_CB_CASE(2) MOE_CB_CASE(3) MOE_CB_CASE(4)
+        MOE_CB_CASE(5) MOE_CB_CASE(6) MOE_CB_CASE(7) MOE_CB_CASE(8)
+        MOE_CB_CASE(9) MOE_CB_CASE(10) MOE_CB_CASE(11) MOE_CB_CASE(12)
+        MOE_CB_CASE(13) MOE_CB_CASE(14) MOE_CB_CASE(15) MOE_CB_CASE(16)
+#undef MOE_CB_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t stream) {
+    if (a.T <= 0) return hipSuccess;
+    return a.bf16 ? launch_dtype<true>(a, stream) : launch_dtype<false>(a, stream);
+}
+
+}  // namespace moe

@@ -56,6 +56,7 @@ int check_config(const moe_config* cfg) {
     if (cfg->hidden < 1 || (int64_t(cfg->hidden) * eb) % 16 != 0) return MOE_ERR_INVALID_ARG;
     if (cfg->num_experts < 1 || cfg->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
     if (cfg->topk < 1 || cfg->topk > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+    if (cfg->flags & ~MOE_FLAG_BACKWARD) return MOE_ERR_INVALID_ARG;
     const int64_t nmax4 = moe_round_up4(cfg->num_max_tokens_per_rank);
     // Slot and row indices are int32; keep one spare layout tile of headroom.
     if (nmax4 * cfg->topk > int64_t(INT32_MAX) - moe::kLayoutTile) return MOE_ERR_INVALID_ARG;
@@ -85,6 +86,12 @@ void plan(const moe_config* cfg, moe_buffers_desc* d) {
     d->s_e = take(d->max_rows * 4);
     d->x_e = take(d->max_rows * d->row_bytes);
     d->y = take(d->nmax4 * d->row_bytes);
+    d->g_e = d->g_s = d->g_x = -1;
+    if (cfg->flags & MOE_FLAG_BACKWARD) {
+        d->g_e = take(d->max_rows * d->row_bytes);
+        d->g_s = take(d->max_rows * 4);
+        d->g_x = take(d->nmax4 * d->row_bytes);
+    }
     d->workspace_bytes = at;
 }
 
@@ -150,6 +157,8 @@ const char* moe_strerror(int status) {
         case MOE_ERR_HIP: return "HIP launch failed";
         case MOE_ERR_STATE:
             return "dispatch/combine does not match the context's latest layout";
+        case MOE_ERR_UNSUPPORTED:
+            return "backward call on a context created without MOE_FLAG_BACKWARD";
         default: return "unknown status";
     }
 }
@@ -325,6 +334,69 @@ int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
     if (moe::launch_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     *d_y_out = a.y;
+    return MOE_OK;
+}
+
+int moe_combine_backward(moe_ctx* ctx, const void* d_grad_y, const void* d_y_expert,
+                         const int32_t* d_row_map, const float* d_scores, int32_t T, int32_t ntpr,
+                         void* stream, void** d_grad_y_expert_out, float** d_grad_scores_out) {
+    if (!ctx || !d_grad_y_expert_out || !d_grad_scores_out) return MOE_ERR_INVALID_ARG;
+    if (!(ctx->cfg.flags & MOE_FLAG_BACKWARD)) return MOE_ERR_UNSUPPORTED;
+    int64_t ntpr4 = 0;
+    const int st = check_call(ctx, T, ntpr, &ntpr4);
+    if (st != MOE_OK) return st;
+    if (T > 0 && (!d_grad_y || !d_y_expert || !d_row_map || !d_scores)) return MOE_ERR_INVALID_ARG;
+    if (d_row_map == at<int32_t>(ctx, ctx->desc.row_map) &&
+        (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4))
+        return MOE_ERR_STATE;
+    moe::CombineBackwardArgs a;
+    a.grad_y = d_grad_y;
+    a.y_e = d_y_expert;
+    a.row_map = d_row_map;
+    a.scores = d_scores;
+    a.T = T;
+    a.K = ctx->cfg.topk;
+    a.chunks = ctx->chunks;
+    a.row_limit = ntpr4 * ctx->cfg.topk;
+    a.bf16 = ctx->cfg.dtype == MOE_BF16;
+    a.grad_y_e = at<void>(ctx, ctx->desc.g_e);
+    a.grad_s = at<float>(ctx, ctx->desc.g_s);
+    if (moe::launch_combine_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    *d_grad_y_expert_out = a.grad_y_e;
+    *d_grad_scores_out = a.grad_s;
+    return MOE_OK;
+}
+
+int moe_dispatch_backward(moe_ctx* ctx, const void* d_grad_x_expert, const int32_t* d_row_map,
+                          int32_t T, int32_t ntpr, void* stream, void** d_grad_x_out) {
+    if (!ctx || !d_grad_x_out) return MOE_ERR_INVALID_ARG;
+    if (!(ctx->cfg.flags & MOE_FLAG_BACKWARD)) return MOE_ERR_UNSUPPORTED;
+    int64_t ntpr4 = 0;
+    const int st = check_call(ctx, T, ntpr, &ntpr4);
+    if (st != MOE_OK) return st;
+    if (T > 0 && (!d_grad_x_expert || !d_row_map)) return MOE_ERR_INVALID_ARG;
+    if (d_row_map == at<int32_t>(ctx, ctx->desc.row_map) &&
+        (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4))
+        return MOE_ERR_STATE;
+    // The gather-sum of the combine with unit weights (scores == nullptr).
+    moe::CombineArgs a;
+    a.y_e = d_grad_x_expert;
+    a.row_map = d_row_map;
+    a.scores = nullptr;
+    a.T = T;
+    a.K = ctx->cfg.topk;
+    a.chunks = ctx->chunks;
+    a.row_limit = ntpr4 * ctx->cfg.topk;
+    a.bf16 = ctx->cfg.dtype == MOE_BF16;
+    a.y = at<void>(ctx, ctx->desc.g_x);
+    a.segments = ctx->tuning.combine_segments;
+    a.block_waves = ctx->tuning.combine_block_waves;
+    a.nontemporal = ctx->tuning.combine_nontemporal != 0;
+    a.store_nontemporal = ctx->tuning.combine_store_nontemporal != 0;
+    if (moe::launch_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    *d_grad_x_out = a.y;
     return MOE_OK;
 }
 

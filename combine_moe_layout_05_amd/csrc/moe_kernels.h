@@ -100,4 +100,19 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
+struct CombineBackwardArgs {
+    const void* grad_y;     // [T][row_bytes]
+    const void* y_e;        // [>= row_limit][row_bytes]
+    const int32_t* row_map; // [T][K]
+    const float* scores;    // [T][K]
+    int32_t T;
+    int32_t K;
+    int32_t chunks;         // row_bytes / 16
+    int64_t row_limit;      // rows >= this (or < 0) count as no expert
+    bool bf16;
+    void* grad_y_e;         // rows r(t,k) written
+    float* grad_s;          // [T][K]
+};
+hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t stream);
+
 }  // namespace moe

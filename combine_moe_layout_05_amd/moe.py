@@ -70,7 +70,7 @@ class MoeDispatcher:
 
     def __init__(self, num_max_tokens_per_rank: int, hidden: int, num_experts: int,
                  topk: int, dtype: torch.dtype = torch.bfloat16,
-                 device: Optional[torch.device] = None):
+                 device: Optional[torch.device] = None, backward: bool = False):
         if dtype not in _DTYPES:
             raise TypeError(f"dtype must be one of {list(_DTYPES)}")
         lib = L.load()
@@ -82,8 +82,9 @@ class MoeDispatcher:
         self.dtype = dtype
         self.hidden, self.num_experts, self.topk = hidden, num_experts, topk
         self.num_max_tokens_per_rank = num_max_tokens_per_rank
+        self.backward_enabled = bool(backward)
         self._cfg = L.MoeConfig(num_max_tokens_per_rank, hidden, num_experts, topk,
-                                _DTYPES[dtype])
+                                _DTYPES[dtype], L.MOE_FLAG_BACKWARD if backward else 0)
         nbytes = C.c_size_t(0)
         L.check(lib.moe_workspace_bytes(C.byref(self._cfg), C.byref(nbytes)),
                 "moe_workspace_bytes")
@@ -105,6 +106,10 @@ class MoeDispatcher:
         self.s_e = self._view(d.s_e, d.max_rows, torch.float32)
         self.x_e = self._view(d.x_e, d.max_rows * D, dtype).view(d.max_rows, D)
         self.y = self._view(d.y, self.nmax4 * D, dtype).view(self.nmax4, D)
+        if backward:
+            self.g_e = self._view(d.g_e, d.max_rows * D, dtype).view(d.max_rows, D)
+            self.g_s = self._view(d.g_s, d.max_rows, torch.float32).view(self.nmax4, K)
+            self.g_x = self._view(d.g_x, self.nmax4 * D, dtype).view(self.nmax4, D)
 
     def _view(self, off: int, n: int, dtype: torch.dtype) -> torch.Tensor:
         nbytes = int(n) * torch.empty(0, dtype=dtype).element_size()
@@ -184,6 +189,55 @@ class MoeDispatcher:
                                       T, ntpr, _stream(self.device), C.byref(out)),
                 "moe_combine")
         return self.y[:T]
+
+    # -- backward ----------------------------------------------------------
+    def _expert_rows(self, t: torch.Tensor, name: str, ntpr: int) -> torch.Tensor:
+        if t.device != self.device or t.dtype != self.dtype:
+            raise TypeError(f"{name} must match the dispatcher's device and dtype")
+        if t.dim() != 2 or t.shape[1] != self.hidden or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [rows, {self.hidden}] tensor")
+        if t.shape[0] < round_up4(ntpr) * self.topk:
+            raise ValueError(f"{name} needs round_up4(num_tokens_per_rank) * topk rows")
+        return t
+
+    def _row_map(self, rm: torch.Tensor, T: int) -> torch.Tensor:
+        if rm.device != self.device or rm.dtype != torch.int32 or not rm.is_contiguous():
+            raise ValueError("row_map must be a contiguous int32 tensor on the device")
+        if rm.dim() != 2 or rm.shape[1] != self.topk or rm.shape[0] < T:
+            raise ValueError(f"row_map must be [>= T, {self.topk}]")
+        return rm
+
+    def combine_backward(self, grad_y: torch.Tensor, y_expert: torch.Tensor,
+                         row_map: torch.Tensor, topk_scores_TK: torch.Tensor, *,
+                         num_tokens_per_rank: Optional[int] = None):
+        """(dL/dy_expert [round_up4(ntpr)*K, D] view, rows [0,total) valid;
+        dL/dscores [T, K] view) for dL/dy = grad_y [T, D]."""
+        s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
+        T = s.shape[0]
+        g = self._dev(grad_y, "grad_y", self.dtype, self.hidden)
+        if g.shape[0] != T:
+            raise ValueError("grad_y and topk_scores_TK need the same T")
+        ntpr = self._ntpr(T, num_tokens_per_rank)
+        ye = self._expert_rows(y_expert, "y_expert", ntpr)
+        rm = self._row_map(row_map, T)
+        out_e, out_s = C.c_void_p(), C.c_void_p()
+        L.check(self._lib.moe_combine_backward(self._ctx, g.data_ptr(), ye.data_ptr(),
+                                               rm.data_ptr(), s.data_ptr(), T, ntpr,
+                                               _stream(self.device), C.byref(out_e),
+                                               C.byref(out_s)), "moe_combine_backward")
+        return self.g_e[:round_up4(ntpr) * self.topk], self.g_s[:T]
+
+    def dispatch_backward(self, grad_x_expert: torch.Tensor, row_map: torch.Tensor, T: int, *,
+                          num_tokens_per_rank: Optional[int] = None) -> torch.Tensor:
+        """dL/dx [T, D] (a view) for dL/dx_expert = grad_x_expert."""
+        ntpr = self._ntpr(T, num_tokens_per_rank)
+        h = self._expert_rows(grad_x_expert, "grad_x_expert", ntpr)
+        rm = self._row_map(row_map, T)
+        out = C.c_void_p()
+        L.check(self._lib.moe_dispatch_backward(self._ctx, h.data_ptr(), rm.data_ptr(), T, ntpr,
+                                                _stream(self.device), C.byref(out)),
+                "moe_dispatch_backward")
+        return self.g_x[:T]
 
     # -- tuning ------------------------------------------------------------
     def set_tuning(self, dispatch_segments: int = 0, combine_segments: int = 0,

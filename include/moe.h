@@ -57,6 +57,10 @@ extern "C" {
 #define MOE_ERR_WORKSPACE   (-3) /* workspace too small or misaligned */
 #define MOE_ERR_HIP         (-4) /* a HIP launch reported an error */
 #define MOE_ERR_STATE       (-5) /* dispatch/combine without a matching layout */
+#define MOE_ERR_UNSUPPORTED (-6) /* backward call on a context without MOE_FLAG_BACKWARD */
+
+/* moe_config.flags */
+#define MOE_FLAG_BACKWARD   1    /* also carve the backward buffers g_e, g_s, g_x */
 
 /* Limits checked at create. */
 #define MOE_MAX_EXPERTS   1024
@@ -72,6 +76,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *   num_experts              E, 1..MOE_MAX_EXPERTS
  *   topk                     K, 1..MOE_MAX_TOPK
  *   dtype                    moe_dtype of hidden states (x, expert output, y)
+ *   flags                    0 or MOE_FLAG_BACKWARD
  * round_up4(num_max_tokens_per_rank) * topk must fit in int32. */
 typedef struct moe_config {
     int32_t num_max_tokens_per_rank;
@@ -79,6 +84,7 @@ typedef struct moe_config {
     int32_t num_experts;
     int32_t topk;
     int32_t dtype;
+    int32_t flags;
 } moe_config;
 
 /* Byte offsets (into the workspace) and sizes of the persistent buffers,
@@ -94,6 +100,10 @@ typedef struct moe_config {
  *   y           dtype [nmax4][D]     combined output; rows [0,T) of a call
  *   block_hist  int32 [max_tiles][round_up4(E)] layout scratch (per-tile
  *                                    histograms)
+ * With MOE_FLAG_BACKWARD (offsets are -1 without it):
+ *   g_e         dtype [nmax4*K][D]   dL/dy_e from moe_combine_backward
+ *   g_s         f32   [nmax4][K]     dL/dscores from moe_combine_backward
+ *   g_x         dtype [nmax4][D]     dL/dx from moe_dispatch_backward
  * nmax4 = round_up4(num_max_tokens_per_rank). */
 typedef struct moe_buffers_desc {
     int64_t workspace_bytes;
@@ -104,6 +114,7 @@ typedef struct moe_buffers_desc {
     int64_t tile_slots;    /* (t,k) slots per layout tile */
     int64_t counts, offsets, row_map, src_map, s_e, x_e, y;
     int64_t block_hist;
+    int64_t g_e, g_s, g_x;
 } moe_buffers_desc;
 
 /* Opaque per-workspace context; host memory only. */
@@ -180,6 +191,41 @@ int moe_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
 int moe_combine(moe_ctx *ctx, const void *d_y_expert, const int32_t *d_row_map,
                 const float *d_topk_scores, int32_t T, int32_t num_tokens_per_rank,
                 void *stream, void **d_y_out);
+
+/* Backward of moe_combine ([NA] "Testing": forward and backward of the
+ * dispatcher are checked bitwise against the equal-count run). For t < T and
+ * every slot with d_row_map[t][k] = r >= 0:
+ *   g_e[r]       = scores[t][k] * d_grad_y[t]   (one fp32 product, rounded to
+ *                                               the element type)
+ *   g_s[t][k]    = <d_grad_y[t], d_y_expert[r]> (fp32, fixed reduction order)
+ * and g_s[t][k] = +0.0 for a slot without an expert. Rows of g_e other than
+ * the slots' rows are not written.
+ *   d_grad_y       [T][D] gradient of the combine output
+ *   d_y_expert     the expert outputs the forward combine read,
+ *                  [>= round_up4(num_tokens_per_rank) * K][D]
+ *   d_row_map, d_topk_scores, T, num_tokens_per_rank: as for moe_combine
+ *                  (the same MOE_ERR_STATE rule for the context's row map)
+ *   *d_grad_y_expert_out  receives the address of g_e ([nmax4*K][D])
+ *   *d_grad_scores_out    receives the address of g_s ([nmax4][K]; rows [0,T))
+ * Needs MOE_FLAG_BACKWARD (MOE_ERR_UNSUPPORTED otherwise). */
+int moe_combine_backward(moe_ctx *ctx, const void *d_grad_y, const void *d_y_expert,
+                         const int32_t *d_row_map, const float *d_topk_scores, int32_t T,
+                         int32_t num_tokens_per_rank, void *stream,
+                         void **d_grad_y_expert_out, float **d_grad_scores_out);
+
+/* Backward of moe_dispatch: for t < T,
+ *   g_x[t] = sum over k = 0..K-1 with d_row_map[t][k] >= 0 of
+ *            d_grad_x_expert[d_row_map[t][k]]
+ * in fp32, ascending k, from +0.0, rounded to the element type (+0.0 for a
+ * token without an expert).
+ *   d_grad_x_expert  gradient of the dispatched rows,
+ *                    [>= round_up4(num_tokens_per_rank) * K][D]
+ *   d_row_map, T, num_tokens_per_rank: as for moe_combine
+ *   *d_grad_x_out    receives the address of g_x ([nmax4][D]; rows [0,T))
+ * Needs MOE_FLAG_BACKWARD (MOE_ERR_UNSUPPORTED otherwise). */
+int moe_dispatch_backward(moe_ctx *ctx, const void *d_grad_x_expert, const int32_t *d_row_map,
+                          int32_t T, int32_t num_tokens_per_rank, void *stream,
+                          void **d_grad_x_out);
 
 /* Launch shape tuning (optional). Each token row is split into `segments`
  * wavefront work items (1..16) and `block_waves` wavefronts (1..16) form a

@@ -1,0 +1,222 @@
+"""GPU parity of the backward entry points (moe_combine_backward,
+moe_dispatch_backward) against the CPU oracle on the same seeded inputs, and
+the pages' bitwise reproduction of the equal-count run in the backward pass.
+
+Bars: the scaled copy dL/dy_e and the gather-sum dL/dx are compared bitwise
+(one fp32 product / an fp32 sum in k order, then the element rounding: the
+same operations on both sides). dL/dscores is a length-D dot product whose
+fp32 evaluation order on the GPU (lane-local, butterfly over lanes, then
+wavefronts) is not the oracle's; it is compared with the oracle's exact fp64
+value within the fp32 summation bound gamma_D * sum_d |g_d * y_d|,
+gamma_D = D u / (1 - D u), u = 2^-24."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from combine_moe_layout_05_amd import MoeDispatcher, MoeError, round_up4
+
+from gpu_util import DEV, ORACLE_THREADS, f32_dev, i32_dev, note, x_to_dev, x_to_np
+
+pytestmark = pytest.mark.gpu
+U32 = 2.0 ** -24
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _grad_y(T, D, dtype, seed):
+    g = np.random.default_rng(seed).standard_normal((T, D)).astype(np.float32)
+    if dtype == "f32":
+        return g
+    return torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _f64(a):
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def gpu_backward(disp, x, ids, scores, g, T, ntpr):
+    """Forward layout + dispatch, identity expert, then both backward calls."""
+    ids_d, s_d = i32_dev(ids[:T]), f32_dev(scores[:T])
+    lay = disp.layout(ids_d, ntpr)
+    dsp = disp.dispatch(x_to_dev(x[:T]), s_d, ids_d, lay.counts, num_tokens_per_rank=ntpr)
+    g_e, g_s = disp.combine_backward(x_to_dev(g[:T]), dsp.x_e, lay.row_map, s_d,
+                                     num_tokens_per_rank=ntpr)
+    g_x = disp.dispatch_backward(g_e, lay.row_map, T, num_tokens_per_rank=ntpr)
+    torch.cuda.synchronize()
+    total = int(lay.offsets[-1].item())
+    return {"g_e": x_to_np(g_e[:total]), "g_s": g_s.cpu().numpy(), "g_x": x_to_np(g_x),
+            "row_map": lay.row_map.cpu().numpy(), "total": total}
+
+
+def oracle_backward(x, ids, scores, g, T, ntpr, E, K):
+    lay = oracle.layout(ids[:T], T, ntpr, E, K)
+    x_e, _ = oracle.dispatch(x[:T], scores[:T], K, lay["src"], ORACLE_THREADS)
+    g_e, g_s = oracle.combine_backward(g[:T], x_e, lay["row_map"], scores[:T], T, K,
+                                       ORACLE_THREADS)
+    g_x = oracle.dispatch_backward(g_e, lay["row_map"], T, K, ORACLE_THREADS)
+    return {"g_e": g_e, "g_s": g_s, "g_x": g_x, "row_map": lay["row_map"],
+            "total": lay["total"], "x_e": x_e}
+
+
+def assert_backward_parity(gb, ob, g, T, K):
+    assert gb["total"] == ob["total"]
+    np.testing.assert_array_equal(gb["row_map"], ob["row_map"])
+    assert np.array_equal(gb["g_e"].view(np.uint8), ob["g_e"].view(np.uint8)), "dL/dy_e"
+    assert np.array_equal(gb["g_x"].view(np.uint8), ob["g_x"].view(np.uint8)), "dL/dx"
+    # dL/dscores within the fp32 dot-product bound of the exact value
+    D = g.shape[1]
+    gamma = D * U32 / (1 - D * U32)
+    G = _f64(g[:T])
+    rm = ob["row_map"][:T]
+    got = gb["g_s"].astype(np.float64)
+    for t0 in range(0, T, 256):
+        t1 = min(T, t0 + 256)
+        for k in range(K):
+            r = rm[t0:t1, k]
+            ok = r >= 0
+            mag = np.zeros(t1 - t0)
+            if ok.any():
+                Y = _f64(ob["x_e"][r[ok]])
+                mag[ok] = np.sum(np.abs(G[t0:t1][ok] * Y), axis=1)
+            err = np.abs(got[t0:t1, k] - ob["g_s"][t0:t1, k])
+            assert np.all(err <= gamma * mag + 1e-30), (t0, k, float(err.max()))
+            # no-expert slots: exactly +0.0
+            assert np.all(gb["g_s"][t0:t1, k][~ok].view(np.uint32) == 0)
+
+
+def _case(name, T=None):
+    w = workloads.WORKLOADS[name]
+    b = workloads.make_batch(w, T=T)
+    g = _grad_y(b["ids"].shape[0], w.D, w.dtype, 77)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=DEV, backward=True)
+    return w, b, g, disp
+
+
+def test_backward_tiny_fp32():
+    w, b, g, disp = _case("tiny")
+    for T in (w.T, 61, 1):
+        note(f"backward tiny T={T}")
+        gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, T, w.ntpr)
+        ob = oracle_backward(b["x"], b["ids"], b["scores"], g, T, w.ntpr, w.E, w.K)
+        assert_backward_parity(gb, ob, g, T, w.K)
+
+
+@pytest.mark.parametrize("T", [5, 614, 2047])
+def test_backward_padded(T):
+    w, b, g, disp = _case("padded")
+    note(f"backward padded T={T}")
+    gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, T, w.ntpr)
+    ob = oracle_backward(b["x"], b["ids"], b["scores"], g, T, w.ntpr, w.E, w.K)
+    assert_backward_parity(gb, ob, g, T, w.K)
+    del disp
+    _free()
+
+
+@pytest.mark.parametrize("name", ["dsv3", "graph"])
+def test_backward_full_shapes(name):
+    w, b, g, disp = _case(name)
+    note(f"backward {name} T={w.T}")
+    gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, w.T, w.ntpr)
+    ob = oracle_backward(b["x"], b["ids"], b["scores"], g, w.T, w.ntpr, w.E, w.K)
+    assert_backward_parity(gb, ob, g, w.T, w.K)
+    note(f"backward {name} repeat")
+    gb2 = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, w.T, w.ntpr)
+    for k in ("g_e", "g_s", "g_x"):
+        assert np.array_equal(gb[k], gb2[k]), k          # deterministic
+    del disp, ob
+    _free()
+
+
+def test_backward_unequal_counts_reproduce_equal_count_run():
+    w, b, g, disp = _case("padded")
+    note("backward padding invariance, full run")
+    full = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, 2048, 2048)
+    frm = full["row_map"][:2048]
+    for T in workloads.PADDED_T_VALUES:
+        note(f"backward padding invariance T={T}")
+        gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, T, 2048)
+        assert np.array_equal(gb["g_s"].view(np.uint32), full["g_s"][:T].view(np.uint32))
+        assert np.array_equal(gb["g_x"], full["g_x"][:T])
+        rm = gb["row_map"][:T].ravel()
+        rf = frm[:T].ravel()
+        assert np.array_equal(gb["g_e"][rm[rm >= 0]], full["g_e"][rf[rf >= 0]])
+    for a, c in workloads.PADDED_PAIRS:
+        ntpr = round_up4(max(a, c))
+        note(f"backward pair {a}&{c}")
+        ga = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, a, ntpr)
+        gc_ = gpu_backward(disp, b["x"][a:], b["ids"][a:], b["scores"][a:], g[a:], c, ntpr)
+        assert np.array_equal(ga["g_x"], full["g_x"][:a])
+        assert np.array_equal(gc_["g_x"], full["g_x"][a:a + c])
+        assert np.array_equal(ga["g_s"], full["g_s"][:a])
+        assert np.array_equal(gc_["g_s"], full["g_s"][a:a + c])
+    del disp
+    _free()
+
+
+def test_backward_edge_cases():
+    rng = np.random.default_rng(9)
+    cases = [  # T, ntpr, nmax, D, E, K, dtype, duplicates/oob
+        (513, 600, 1000, 256, 16, 6, "bf16", True),
+        (300, 300, 300, 64, 1024, 16, "bf16", False),
+        (77, 80, 80, 36, 8, 3, "f32", True),
+        (123, 123, 130, 200, 32, 8, "bf16", False),
+        (9, 9, 9, 8, 1, 1, "bf16", False),
+    ]
+    for T, ntpr, nmax, D, E, K, dtype, messy in cases:
+        if messy:
+            ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+            m = rng.random((T, K)) < 0.1
+            ids[m] = rng.choice(np.array([-1, E, -3], np.int32), size=int(m.sum()))
+        else:
+            ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+        ids[0, :] = -1                                   # one token without an expert
+        scores = rng.standard_normal((T, K)).astype(np.float32)
+        xf = rng.standard_normal((T, D)).astype(np.float32)
+        x = xf if dtype == "f32" else \
+            torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        g = _grad_y(T, D, dtype, 6)
+        disp = MoeDispatcher(nmax, D, E, K, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                             device=DEV, backward=True)
+        note(f"backward edge T={T} ntpr={ntpr} D={D} E={E} K={K} {dtype}")
+        gb = gpu_backward(disp, x, ids, scores, g, T, ntpr)
+        ob = oracle_backward(x, ids, scores, g, T, ntpr, E, K)
+        assert_backward_parity(gb, ob, g, T, K)
+        assert (gb["g_x"][0].view(np.uint8) == 0).all()       # +0.0
+        assert (gb["g_s"][0].view(np.uint32) == 0).all()
+
+
+def test_backward_poisoned_workspace_and_flag():
+    w = workloads.WORKLOADS["padded"]
+    b = workloads.make_batch(w)
+    g = _grad_y(2048, w.D, "bf16", 8)
+    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV, backward=True)
+    disp.workspace.fill_(0xFF)
+    torch.cuda.synchronize()
+    T = 614
+    note("backward poison T=614")
+    gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, T, w.ntpr)
+    ob = oracle_backward(b["x"], b["ids"], b["scores"], g, T, w.ntpr, w.E, w.K)
+    assert_backward_parity(gb, ob, g, T, w.K)
+    assert bool((disp.g_e[ob["total"]:].view(torch.int16) == -1).all())   # not written
+    assert bool((disp.g_x[T:].view(torch.int16) == -1).all())
+    del disp
+    plain = MoeDispatcher(64, 128, 8, 2, dtype=torch.float32, device=DEV)
+    ids = i32_dev(np.zeros((4, 2), np.int32))
+    s = f32_dev(np.ones((4, 2), np.float32))
+    lay = plain.layout(ids, 4)
+    with pytest.raises(AttributeError):
+        plain.g_e
+    with pytest.raises(MoeError):
+        plain.dispatch_backward(plain.x_e, lay.row_map, 4)
+    torch.cuda.synchronize()
+    _free()

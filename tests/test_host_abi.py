@@ -56,8 +56,8 @@ def test_capacity_helpers_agree_with_oracle(lib):
                        (oracle.check_capacity(T, ntpr, nmax) == 0)
 
 
-def _cfg(nmax=4096, D=7168, E=256, K=8, dtype=L.MOE_BF16):
-    return L.MoeConfig(nmax, D, E, K, dtype)
+def _cfg(nmax=4096, D=7168, E=256, K=8, dtype=L.MOE_BF16, flags=0):
+    return L.MoeConfig(nmax, D, E, K, dtype, flags)
 
 
 def _bytes(lib, cfg):
@@ -78,15 +78,18 @@ def test_config_validation(lib):
     assert _bytes(lib, _cfg(K=L.MOE_MAX_TOPK + 1))[0] == L.MOE_ERR_INVALID_ARG
     assert _bytes(lib, _cfg(dtype=7))[0] == L.MOE_ERR_INVALID_ARG
     assert _bytes(lib, _cfg(nmax=2**31 - 1, K=16))[0] == L.MOE_ERR_INVALID_ARG  # int32 rows
+    assert _bytes(lib, _cfg(flags=2))[0] == L.MOE_ERR_INVALID_ARG              # unknown flag
+    assert _bytes(lib, _cfg(flags=L.MOE_FLAG_BACKWARD))[0] == L.MOE_OK
     assert lib.moe_workspace_bytes(None, None) == L.MOE_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("flags", [0, L.MOE_FLAG_BACKWARD])
 @pytest.mark.parametrize("nmax,D,E,K,dtype", [
     (4096, 7168, 256, 8, L.MOE_BF16), (64, 128, 8, 2, L.MOE_F32),
     (4097, 2048, 128, 8, L.MOE_BF16), (32768, 7168, 256, 8, L.MOE_BF16),
     (1, 8, 1, 1, L.MOE_BF16), (8192, 4096, 1024, 16, L.MOE_BF16)])
-def test_workspace_carve_up(lib, nmax, D, E, K, dtype):
-    cfg = _cfg(nmax, D, E, K, dtype)
+def test_workspace_carve_up(lib, nmax, D, E, K, dtype, flags):
+    cfg = _cfg(nmax, D, E, K, dtype, flags)
     st, nbytes = _bytes(lib, cfg)
     assert st == L.MOE_OK
     fake = 1 << 40                                   # never dereferenced on the host
@@ -100,6 +103,10 @@ def test_workspace_carve_up(lib, nmax, D, E, K, dtype):
     sizes = {"counts": E * 4, "offsets": (E + 1) * 4, "row_map": n4 * K * 4,
              "src_map": n4 * K * 4, "s_e": n4 * K * 4, "x_e": n4 * K * D * eb,
              "y": n4 * D * eb, "block_hist": d.max_tiles * oracle.round_up4(E) * 4}
+    if flags & L.MOE_FLAG_BACKWARD:
+        sizes.update(g_e=n4 * K * D * eb, g_s=n4 * K * 4, g_x=n4 * D * eb)
+    else:
+        assert d.g_e == d.g_s == d.g_x == -1
     assert d.max_tiles * d.tile_slots >= n4 * K
     spans = sorted((getattr(d, k), getattr(d, k) + v, k) for k, v in sizes.items())
     for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
@@ -158,6 +165,30 @@ def test_calls_reject_bad_arguments_before_enqueueing(lib):
     lib.moe_destroy(ctx)
 
 
+def test_backward_calls_need_the_flag_and_a_matching_layout(lib):
+    out_e, out_s, out_x = C.c_void_p(), C.c_void_p(), C.c_void_p()
+    p = 1 << 41
+    ctx, d, _ = _ctx(lib, _cfg(4096, 2048, 128, 8, L.MOE_BF16))
+    assert lib.moe_combine_backward(ctx, p, p, p, p, 5, 8, None, C.byref(out_e),
+                                    C.byref(out_s)) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_dispatch_backward(ctx, p, p, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_UNSUPPORTED
+    lib.moe_destroy(ctx)
+    ctx, d, _ = _ctx(lib, _cfg(4096, 2048, 128, 8, L.MOE_BF16, L.MOE_FLAG_BACKWARD))
+    rm = (1 << 40) + d.row_map
+    assert lib.moe_combine_backward(ctx, p, p, rm, p, 5, 8, None, C.byref(out_e),
+                                    C.byref(out_s)) == L.MOE_ERR_STATE
+    assert lib.moe_dispatch_backward(ctx, p, rm, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_STATE
+    assert lib.moe_combine_backward(ctx, p, p, p, p, 9, 8, None, C.byref(out_e),
+                                    C.byref(out_s)) == L.MOE_ERR_CAPACITY
+    assert lib.moe_combine_backward(ctx, None, p, p, p, 5, 8, None, C.byref(out_e),
+                                    C.byref(out_s)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_backward(ctx, p, p, p, p, 5, 8, None, None,
+                                    C.byref(out_s)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_backward(ctx, None, p, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_backward(ctx, p, p, 5, 4097, None, C.byref(out_x)) == L.MOE_ERR_CAPACITY
+    lib.moe_destroy(ctx)
+
+
 def test_tuning_roundtrip_and_limits(lib):
     ctx, _, _ = _ctx(lib, _cfg())
     t = L.MoeTuning()
@@ -187,7 +218,7 @@ def test_tuning_roundtrip_and_limits(lib):
 
 
 def test_strerror_covers_every_status(lib):
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         msg = lib.moe_strerror(st).decode()
         assert msg and msg != "unknown status"
     assert lib.moe_strerror(-99).decode() == "unknown status"
