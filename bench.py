@@ -57,6 +57,8 @@ def parse_args():
                    help="1/0 forces combine's streaming loads on/off; -1 keeps the default")
     p.add_argument("--dispatch-block-waves", type=int, default=0)
     p.add_argument("--combine-block-waves", type=int, default=0)
+    p.add_argument("--backward", type=int, default=0,
+                   help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run plain device write/read/copy of this size (HBM ceiling, "
                         "counter scaling)")
@@ -73,7 +75,12 @@ def bytes_per_token(w, kind: str) -> int:
     K = w.K
     return {"layout": 12 * K,
             "dispatch": row * (K + 1) + 12 * K,
-            "combine": row * (K + 1) + 8 * K}[kind]
+            "combine": row * (K + 1) + 8 * K,
+            # read dL/dy row and K expert rows, write K scaled rows; row_map,
+            # scores in, dL/dscores out
+            "combine_backward": row * (2 * K + 1) + 12 * K,
+            # read K rows, write one; row_map in
+            "dispatch_backward": row * (K + 1) + 4 * K}[kind]
 
 
 def source_digest(kind: str) -> str:
@@ -160,7 +167,8 @@ def main() -> int:
         x = torch.from_numpy(b["x"]).to(dev)
     ids = torch.from_numpy(b["ids"]).to(dev)
     s = torch.from_numpy(b["scores"]).to(dev)
-    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=dev)
+    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=dev,
+                         backward=args.backward > 0)
     disp.set_tuning(args.dispatch_segments, args.combine_segments,
                     bool(args.dispatch_nontemporal) if args.dispatch_nontemporal >= 0 else None,
                     bool(args.combine_nontemporal) if args.combine_nontemporal >= 0 else None,
@@ -264,6 +272,31 @@ def main() -> int:
         cold["combine_gbps"] = bytes_per_token(w, "combine") * w.T / (cold["combine_us"] * 1e-6) / 1e9
         log(f"cold: dispatch {cold['dispatch_us']:.1f} us, combine {cold['combine_us']:.1f} us")
 
+    backward = None
+    if args.backward > 0:
+        log(f"backward: {args.backward} timed steps")
+        gy = torch.randn((w.T, w.D), generator=torch.Generator(device=dev).manual_seed(5),
+                         device=dev).to(dt)
+        lay = disp.layout(ids, ntpr)
+        disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.backward + 2)]
+        for e in bev:
+            e[0].record()
+            g_e, _ = disp.combine_backward(gy, disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
+            e[1].record()
+            disp.dispatch_backward(g_e, lay.row_map, w.T, num_tokens_per_rank=ntpr)
+            e[2].record()
+        torch.cuda.synchronize()
+        cb = float(np.mean([e[0].elapsed_time(e[1]) for e in bev[2:]])) * 1e3
+        db = float(np.mean([e[1].elapsed_time(e[2]) for e in bev[2:]])) * 1e3
+        backward = {"combine_backward_us": round(cb, 2), "dispatch_backward_us": round(db, 2),
+                    "combine_backward_gbps": round(bytes_per_token(w, "combine_backward") * w.T
+                                                   / (cb * 1e-6) / 1e9, 1),
+                    "dispatch_backward_gbps": round(bytes_per_token(w, "dispatch_backward") * w.T
+                                                    / (db * 1e-6) / 1e9, 1)}
+        log(f"backward: combine_backward {cb:.1f} us, dispatch_backward {db:.1f} us")
+
     dominant = "dispatch" if avg["dispatch"] >= avg["combine"] else "combine"
     per_launch = bytes_per_token(w, dominant) * w.T
     achieved = per_launch / (avg[dominant] * 1e-3) / 1e9
@@ -321,6 +354,7 @@ def main() -> int:
         },
         "cold_cache": cold,
         "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
+        "backward": backward,
     }
     print(json.dumps(out), flush=True)
     return 0
