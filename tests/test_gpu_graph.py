@@ -127,3 +127,78 @@ def test_graph_replays_with_fresh_routing(cap, chunk):
             np.testing.assert_array_equal(ce, o2["counts"])
             np.testing.assert_array_equal(oe, o2["offsets"])
             assert np.array_equal(ye, o2["y"])
+
+
+def test_graph_buckets_with_different_capacities_share_one_context():
+    """Two graphs captured on one context at capacities 2048 and 8192 ("Unify
+    expert parallel token dispatcher API", section "API design": different
+    graph buckets may use different current capacities over the same
+    storage), each holding forward and backward; replays alternate with fresh
+    routing and every replay matches the oracle."""
+    N, D, E, K = 8192, 1024, 64, 8
+    disp = MoeDispatcher(N, D, E, K, dtype=torch.bfloat16, device=DEV, backward=True)
+    w = workloads.Workload("buckets", T=N, ntpr=N, nmax=N, D=D, E=E, K=K, dtype="bf16",
+                           routing="zipf", zipf_s=1.1, seed=0)
+    graphs = {}
+    for n in (2048, 8192):
+        st = {"x": torch.zeros((n, D), dtype=torch.bfloat16, device=DEV),
+              "ids": torch.full((n, K), -1, dtype=torch.int32, device=DEV),
+              "s": torch.zeros((n, K), dtype=torch.float32, device=DEV),
+              "gy": torch.zeros((n, D), dtype=torch.bfloat16, device=DEV)}
+
+        def body(st=st, n=n):
+            lay = disp.layout(st["ids"], n)
+            disp.dispatch(st["x"], st["s"], st["ids"], lay.counts, num_tokens_per_rank=n)
+            y = disp.combine(disp.x_e, lay.row_map, st["s"], num_tokens_per_rank=n)
+            g_e, g_s = disp.combine_backward(st["gy"], disp.x_e, lay.row_map, st["s"],
+                                             num_tokens_per_rank=n)
+            g_x = disp.dispatch_backward(g_e, lay.row_map, n, num_tokens_per_rank=n)
+            return y, g_s, g_x
+
+        side = torch.cuda.Stream(device=DEV)
+        side.wait_stream(torch.cuda.current_stream(DEV))
+        with torch.cuda.stream(side):
+            body()
+        torch.cuda.current_stream(DEV).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            outs = body()
+        torch.cuda.synchronize()
+        graphs[n] = (g, st, outs)
+
+    rng = np.random.default_rng(31)
+    for i in range(10):
+        n = (2048, 8192)[i % 2]
+        g, st, (y, g_s, g_x) = graphs[n]
+        T = int(rng.integers(1, n + 1))
+        b = workloads.make_batch(w, T=T, seed=700 + i)
+        gy = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
+        gy_bits = gy.view(torch.int16).numpy().view(np.uint16)
+        st["x"][:T].copy_(x_to_dev(b["x"]))
+        st["x"][T:].zero_()
+        st["ids"][:T].copy_(i32_dev(b["ids"]))
+        st["ids"][T:].fill_(-1)
+        st["s"][:T].copy_(f32_dev(b["scores"]))
+        st["s"][T:].zero_()
+        st["gy"][:T].copy_(x_to_dev(gy_bits))
+        st["gy"][T:].zero_()
+        note(f"bucket {n} replay {i} T={T}")
+        g.replay()
+        torch.cuda.synchronize()
+        o = oracle.run_pipeline(b["x"], b["ids"], b["scores"], T, T, E, K, nthreads=ORACLE_THREADS)
+        assert np.array_equal(x_to_np(y)[:T], o["y"])
+        assert (x_to_np(y)[T:] == 0).all()
+        ge_o, gs_o = oracle.combine_backward(gy_bits, o["x_e"], o["row_map"], b["scores"], T, K)
+        gx_o = oracle.dispatch_backward(ge_o, o["row_map"], T, K)
+        assert np.array_equal(x_to_np(g_x)[:T], gx_o)
+        got = g_s.cpu().numpy()[:T].astype(np.float64)
+        G = (gy_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        Y = (o["x_e"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rm = o["row_map"][:T]
+        gamma = D * 2.0 ** -24 / (1 - D * 2.0 ** -24)
+        for k in range(K):
+            mag = np.sum(np.abs(G * Y[rm[:, k]]), axis=1)
+            assert np.all(np.abs(got[:, k] - gs_o[:, k]) <= gamma * mag + 1e-30)
+    del graphs, disp
+    torch.cuda.empty_cache()
