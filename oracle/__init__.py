@@ -11,5 +11,5 @@ from .oracle import (  # noqa: F401
     build_oracle, lib_path, ceil_div, round_up4, num_max_pretrain,
     num_max_infer, validate_num_max, check_capacity, layout, dispatch,
     dispatch_rows, combine, combine_tokens, f32_to_bf16, run_pipeline,
-    combine_backward, dispatch_backward,
+    combine_backward, dispatch_backward, topk_from_routing_map, dispatch_scaled,
 )

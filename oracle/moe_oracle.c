@@ -341,3 +341,51 @@ void orc_dispatch_backward(const void *h, int dtype, int64_t D,
         }
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Input and weighting variants ([NA] "Fix": HybridEP's dispatcher takes a
+ * boolean routing map [T][E] with probabilities [T][E]; padded rows are
+ * all-False with zero probabilities).                                    */
+
+/* Top-k form of a routing map: slot k of token t is the k-th expert e in
+ * ascending order with map[t][e] != 0, score probs[t][e]; slots past the
+ * token's experts get id -1 and score 0. n_experts[t] = number of experts
+ * in the row (a row with more than K keeps its K lowest). */
+void orc_topk_from_routing_map(const uint8_t *map, const float *probs, int64_t T,
+                               int32_t E, int32_t K, int32_t *ids, float *scores,
+                               int32_t *n_experts)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t n = 0;
+        for (int32_t e = 0; e < E; ++e) {
+            if (!map[t * E + e]) continue;
+            if (n < K) {
+                ids[t * K + n] = e;
+                memcpy(&scores[t * K + n], &probs[t * E + e], sizeof(float));
+            }
+            ++n;
+        }
+        for (int32_t k = n; k < K; ++k) {
+            ids[t * K + k] = -1;
+            scores[t * K + k] = 0.0f;
+        }
+        n_experts[t] = n;
+    }
+}
+
+/* Dispatch with the scores applied: x_e[r] = s[t][k] * x[t], one fp32
+ * product rounded to the element dtype, for rows [0,total). */
+void orc_dispatch_scaled(const void *x, int dtype, int64_t D, const float *scores,
+                         int32_t K, const int32_t *src, int64_t total, void *x_e,
+                         int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t r = 0; r < total; ++r) {
+        int64_t slot = src[r];
+        int64_t t = slot / K;
+        float s = scores[slot];
+        for (int64_t d = 0; d < D; ++d)
+            orc_store_elem(x_e, dtype, r * D + d, s * orc_load_elem(x, dtype, t * D + d));
+    }
+}

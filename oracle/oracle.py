@@ -66,6 +66,10 @@ def _load():
         L.orc_combine_backward.restype = None
         L.orc_dispatch_backward.argtypes = [vp, C.c_int, i64, vp, i64, i32, vp, C.c_int]
         L.orc_dispatch_backward.restype = None
+        L.orc_topk_from_routing_map.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
+        L.orc_topk_from_routing_map.restype = None
+        L.orc_dispatch_scaled.argtypes = [vp, C.c_int, i64, vp, i32, vp, i64, vp, C.c_int]
+        L.orc_dispatch_scaled.restype = None
         _lib = L
         return L
 
@@ -246,3 +250,34 @@ def dispatch_backward(h: np.ndarray, row_map: np.ndarray, T: int, K: int,
         L.orc_dispatch_backward(_ptr(h_arg), _dtype_code(h), D, _ptr(row_map), T, K,
                                 _ptr(gx), nthreads)
     return gx
+
+
+def topk_from_routing_map(routing_map: np.ndarray, probs: np.ndarray, K: int):
+    """(ids [T, K] int32, scores [T, K] float32, n_experts [T] int32)."""
+    L = _load()
+    m = np.ascontiguousarray(routing_map).astype(np.uint8, copy=False)
+    m = np.ascontiguousarray(m)
+    probs = np.ascontiguousarray(probs, dtype=np.float32)
+    T, E = m.shape
+    ids = np.empty((T, K), np.int32)
+    scores = np.empty((T, K), np.float32)
+    n = np.empty(T, np.int32)
+    if T:
+        L.orc_topk_from_routing_map(_ptr(m), _ptr(probs), T, E, K, _ptr(ids), _ptr(scores),
+                                    _ptr(n))
+    return ids, scores, n
+
+
+def dispatch_scaled(x: np.ndarray, scores: np.ndarray, K: int, src: np.ndarray,
+                    nthreads: int = 1) -> np.ndarray:
+    """x_e [total, D]: row r = scores[slot] * x[slot // K], rounded."""
+    L = _load()
+    x = np.ascontiguousarray(x)
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    src = np.ascontiguousarray(src, dtype=np.int32)
+    D = x.shape[1]
+    x_e = np.empty((src.size, D), x.dtype)
+    if src.size:
+        L.orc_dispatch_scaled(_ptr(x), _dtype_code(x), D, _ptr(scores), K, _ptr(src), src.size,
+                              _ptr(x_e), nthreads)
+    return x_e

@@ -619,3 +619,91 @@ def test_backward_unequal_counts_reproduce_equal_count_run():
         assert np.array_equal(gx, gx_f[:T])
         rm, rmf = lay["row_map"][:T].ravel(), lay_f["row_map"][:T].ravel()
         assert np.array_equal(ge[rm[rm >= 0]], ge_f[rmf[rmf >= 0]])   # per slot
+
+
+# --------------------------------------------------------------------------
+# Routing-map input format and scores applied on dispatch
+
+def _map_from_topk(ids, probs_src, E):
+    T, K = ids.shape
+    m = np.zeros((T, E), np.uint8)
+    p = np.zeros((T, E), np.float32)
+    rows = np.repeat(np.arange(T), K)
+    flat = ids.ravel()
+    ok = flat >= 0
+    m[rows[ok], flat[ok]] = 1
+    p[rows[ok], flat[ok]] = probs_src.ravel()[ok]
+    return m, p
+
+
+def test_routing_map_round_trip_and_padding_rows():
+    rng = np.random.default_rng(41)
+    T, E, K = 200, 64, 8
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    ids[rng.random((T, K)) < 0.1] = -1
+    ids[-7:] = -1                                   # padded rows: all-False, zero probs
+    scores = rng.random((T, K)).astype(np.float32)
+    m, p = _map_from_topk(ids, scores, E)
+    got_ids, got_s, n = oracle.topk_from_routing_map(m, p, K)
+    for t in range(T):
+        valid = np.sort(ids[t][ids[t] >= 0])
+        assert n[t] == valid.size
+        assert got_ids[t, :valid.size].tolist() == valid.tolist()       # ascending experts
+        assert (got_ids[t, valid.size:] == -1).all()
+        assert np.array_equal(got_s[t, :valid.size], p[t, valid])
+        assert (got_s[t, valid.size:] == 0).all()
+    assert (n[-7:] == 0).all() and (got_ids[-7:] == -1).all()
+
+
+def test_routing_map_row_with_more_than_k_experts_keeps_the_lowest():
+    m = np.zeros((2, 10), np.uint8)
+    m[0, [1, 3, 4, 7, 9]] = 1
+    p = np.arange(20, dtype=np.float32).reshape(2, 10) / 8
+    ids, s, n = oracle.topk_from_routing_map(m, p, 3)
+    assert ids.tolist() == [[1, 3, 4], [-1, -1, -1]]
+    assert s[0].tolist() == [p[0, 1], p[0, 3], p[0, 4]] and n.tolist() == [5, 0]
+
+
+def test_routing_map_layout_matches_topk_layout_per_expert():
+    # Both formats put the same tokens in each expert's segment, in token order.
+    w = workloads.WORKLOADS["padded"]
+    b = workloads.make_batch(w, with_x=False)
+    T = 777
+    m, p = _map_from_topk(b["ids"][:T], b["scores"][:T], w.E)
+    ids2, s2, n = oracle.topk_from_routing_map(m, p, w.K)
+    a = oracle.layout(b["ids"][:T], T, T, w.E, w.K)
+    c = oracle.layout(ids2, T, T, w.E, w.K)
+    np.testing.assert_array_equal(a["counts"], c["counts"])
+    np.testing.assert_array_equal(a["offsets"], c["offsets"])
+    np.testing.assert_array_equal(a["src"] // w.K, c["src"] // w.K)
+    # and the slot scores travel with their experts
+    sa = b["scores"][:T].ravel()[a["src"]]
+    sc = s2.ravel()[c["src"]]
+    assert np.array_equal(sa, sc)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dispatch_scaled_is_one_rounded_product(dtype):
+    w = workloads.Workload("sc", T=300, ntpr=300, nmax=300, D=48, E=32, K=4, dtype=dtype,
+                           routing="uniform", seed=4)
+    b = workloads.make_batch(w)
+    lay = oracle.layout(b["ids"], w.T, w.ntpr, w.E, w.K)
+    x_e = oracle.dispatch_scaled(b["x"], b["scores"], w.K, lay["src"])
+    t = lay["src"] // w.K
+    s = b["scores"].ravel()[lay["src"]]
+    xf = b["x"].astype(np.float32) if dtype == "f32" else \
+        (b["x"].astype(np.uint32) << 16).view(np.float32)
+    prod = (s[:, None].astype(np.float32) * xf[t]).astype(np.float32)   # fp32 product
+    want = prod if dtype == "f32" else _torch_bf16_bits(prod)
+    assert np.array_equal(x_e, want)
+
+
+def test_scaled_dispatch_with_unit_combine_matches_weighted_combine_when_exact():
+    T, D, E, K = 40, 64, 8, 4
+    x, ids, scores = _dyadic_inputs(T, D, 9)
+    lay = oracle.layout(ids, T, T, E, K)
+    xs = oracle.dispatch_scaled(x, scores, K, lay["src"])
+    y_unit = oracle.combine(xs, lay["row_map"], np.ones((T, K), np.float32), T, K)
+    x_e, _ = oracle.dispatch(x, scores, K, lay["src"])
+    y_w = oracle.combine(x_e, lay["row_map"], scores, T, K)
+    assert np.array_equal(y_unit, y_w)
