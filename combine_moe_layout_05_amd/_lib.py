@@ -43,7 +43,7 @@ class MoeBuffersDesc(C.Structure):
     _fields_ = [(n, _i64) for n in (
         "workspace_bytes", "nmax4", "max_rows", "row_bytes", "max_tiles", "tile_slots",
         "counts", "offsets", "row_map", "src_map", "s_e", "x_e", "y",
-        "block_hist", "g_e", "g_s", "g_x")]
+        "block_hist", "map_ids", "map_scores", "map_n_experts", "g_e", "g_s", "g_x")]
 
 
 class MoeTuning(C.Structure):
@@ -61,6 +61,9 @@ SIGNATURES = {
     "moe_layout": (_int, [_vp, _vp, _i32, _i32, _vp]),
     "moe_dispatch": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "moe_combine": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
+    "moe_dispatch_scaled": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+    "moe_topk_from_routing_map": (_int, [_vp, _vp, _vp, _i32, _vp, C.POINTER(_vp),
+                                         C.POINTER(_vp), C.POINTER(_vp)]),
     "moe_combine_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp),
                                     C.POINTER(_vp)]),
     "moe_dispatch_backward": (_int, [_vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "combine_backward.hip", "moe_api.cpp"]
+SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "combine_backward.hip", "routing_map.hip",
+           "moe_api.cpp"]
 HEADERS = [os.path.join(CSRC, "moe_kernels.h"), os.path.join(CSRC, "moe_lanes.h"),
            os.path.join(INCLUDE, "moe.h")]
 

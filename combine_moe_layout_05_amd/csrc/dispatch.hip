@@ -23,11 +23,10 @@
 // workgroup barrier beats per-wavefront scalar loads of the row map by ~9 %,
 // because the barrier lines the wavefronts up on neighbouring pieces.)
 #include "moe_kernels.h"
+#include "moe_lanes.h"
 
 namespace moe {
 namespace {
-
-typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kDispatchUnroll = 4;   // 16-byte chunks per lane in flight
 
@@ -39,10 +38,22 @@ __device__ __forceinline__ void put(v4i* p, v4i v) {
         *p = v;
 }
 
+// Row transform of a dispatch: a bit copy, or the slot's score applied (one
+// fp32 product rounded to the element type).
+enum RowMode { kCopy = 0, kScaleF32 = 1, kScaleBF16 = 2 };
+
+template <int MODE>
+__device__ __forceinline__ v4i transform(float s, v4i v) {
+    if constexpr (MODE == kCopy)
+        return v;
+    else
+        return Lanes<MODE == kScaleBF16>::scale(s, v);
+}
+
 // One wavefront per (token, row segment). SINGLE: the segment is exactly one
 // 16-byte chunk per lane (the default launch shape); otherwise the segment is
 // copied in groups of U chunks per lane, then one chunk at a time.
-template <int K, bool NT, bool SINGLE>
+template <int K, bool NT, bool SINGLE, int MODE>
 __global__ __launch_bounds__(kMaxBlockThreads)
 void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores,
                      const int32_t* __restrict__ row_map, int32_t T, int32_t chunks,
@@ -53,6 +64,7 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     // barrier. The barrier also starts the workgroup's wavefronts together, so
     // they store neighbouring 1 KiB pieces of the same rows at the same time.
     __shared__ int32_t tile_rows[kMaxBlockWaves * K];
+    __shared__ float tile_scores[kMaxBlockWaves * K];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -64,7 +76,9 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     const int staged = static_cast<int>(t_last - t_first + 1) * K;
     if (tid < staged) {
         const int32_t r = row_map[t_first * K + tid];
-        tile_rows[tid] = (r >= 0 && r < max_rows) ? r : -1;
+        const bool ok = r >= 0 && r < max_rows;
+        tile_rows[tid] = ok ? r : -1;
+        if constexpr (MODE != kCopy) tile_scores[tid] = ok ? scores[t_first * K + tid] : 0.0f;
     }
     __syncthreads();
 
@@ -74,8 +88,15 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     const int seg = static_cast<int>(item - t * segments);
     const int32_t* rows = tile_rows + (t - t_first) * K;
     int32_t row[K];
+    float s[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) row[k] = __builtin_amdgcn_readfirstlane(rows[k]);
+    for (int k = 0; k < K; ++k) {
+        row[k] = __builtin_amdgcn_readfirstlane(rows[k]);
+        s[k] = 0.0f;
+        if constexpr (MODE != kCopy)
+            s[k] = __int_as_float(__builtin_amdgcn_readfirstlane(
+                __float_as_int(tile_scores[(t - t_first) * K + k])));
+    }
 
     const int32_t c_begin = seg * seg_chunks;
     const int32_t c_end = min(c_begin + seg_chunks, chunks);
@@ -98,7 +119,7 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
         if (in) {
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, v);
+                if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, transform<MODE>(s[k], v));
         }
     } else {
         move_score();
@@ -113,7 +134,7 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
                 if (row[k] < 0) continue;
                 v4i* dst = x_e + int64_t(row[k]) * chunks + c0 + lane;
 #pragma unroll
-                for (int u = 0; u < U; ++u) put<NT>(dst + u * 64, v[u]);
+                for (int u = 0; u < U; ++u) put<NT>(dst + u * 64, transform<MODE>(s[k], v[u]));
             }
         }
         // Tail: one chunk per lane at a time, the last possibly partial.
@@ -123,7 +144,7 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
             const v4i v = src[c];
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, v);
+                if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, transform<MODE>(s[k], v));
         }
     }
 }
@@ -134,10 +155,18 @@ hipError_t launch_k(const DispatchArgs& a, int32_t segments, int32_t seg_chunks,
     const int64_t items = int64_t(a.T) * segments;
     const int64_t blocks = (items + a.block_waves - 1) / a.block_waves;
     const bool single = seg_chunks == 64;
-    auto kernel = a.nontemporal ? (single ? dispatch_kernel<K, true, true>
-                                          : dispatch_kernel<K, true, false>)
-                                : (single ? dispatch_kernel<K, false, true>
-                                          : dispatch_kernel<K, false, false>);
+    decltype(&dispatch_kernel<K, false, true, kCopy>) kernel;
+    if (a.scaled) {  // streaming stores are not offered with the scores applied
+        kernel = a.bf16 ? (single ? dispatch_kernel<K, false, true, kScaleBF16>
+                                  : dispatch_kernel<K, false, false, kScaleBF16>)
+                        : (single ? dispatch_kernel<K, false, true, kScaleF32>
+                                  : dispatch_kernel<K, false, false, kScaleF32>);
+    } else {
+        kernel = a.nontemporal ? (single ? dispatch_kernel<K, true, true, kCopy>
+                                         : dispatch_kernel<K, true, false, kCopy>)
+                               : (single ? dispatch_kernel<K, false, true, kCopy>
+                                         : dispatch_kernel<K, false, false, kCopy>);
+    }
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * a.block_waves), 0,
                        stream, static_cast<const v4i*>(a.x), a.scores, a.row_map, a.T,
                        a.chunks, segments, seg_chunks, a.max_rows, static_cast<v4i*>(a.x_e),

@@ -86,6 +86,9 @@ void plan(const moe_config* cfg, moe_buffers_desc* d) {
     d->s_e = take(d->max_rows * 4);
     d->x_e = take(d->max_rows * d->row_bytes);
     d->y = take(d->nmax4 * d->row_bytes);
+    d->map_ids = take(d->max_rows * 4);
+    d->map_scores = take(d->max_rows * 4);
+    d->map_n_experts = take(d->nmax4 * 4);
     d->g_e = d->g_s = d->g_x = -1;
     if (cfg->flags & MOE_FLAG_BACKWARD) {
         d->g_e = take(d->max_rows * d->row_bytes);
@@ -279,8 +282,9 @@ int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
     return MOE_OK;
 }
 
-int moe_dispatch(moe_ctx* ctx, const void* d_x, const float* d_scores, const int32_t* d_ids,
-                 const int32_t* d_counts, int32_t T, int32_t ntpr, void* stream) {
+static int dispatch_impl(moe_ctx* ctx, const void* d_x, const float* d_scores,
+                         const int32_t* d_ids, const int32_t* d_counts, int32_t T, int32_t ntpr,
+                         void* stream, bool scaled) {
     if (!ctx) return MOE_ERR_INVALID_ARG;
     int64_t ntpr4 = 0;
     const int st = check_call(ctx, T, ntpr, &ntpr4);
@@ -302,8 +306,45 @@ int moe_dispatch(moe_ctx* ctx, const void* d_x, const float* d_scores, const int
     a.segments = ctx->tuning.dispatch_segments;
     a.block_waves = ctx->tuning.dispatch_block_waves;
     a.nontemporal = ctx->tuning.dispatch_nontemporal != 0;
+    a.scaled = scaled;
+    a.bf16 = ctx->cfg.dtype == MOE_BF16;
     if (moe::launch_dispatch(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_dispatch(moe_ctx* ctx, const void* d_x, const float* d_scores, const int32_t* d_ids,
+                 const int32_t* d_counts, int32_t T, int32_t ntpr, void* stream) {
+    return dispatch_impl(ctx, d_x, d_scores, d_ids, d_counts, T, ntpr, stream, false);
+}
+
+int moe_dispatch_scaled(moe_ctx* ctx, const void* d_x, const float* d_scores,
+                        const int32_t* d_ids, const int32_t* d_counts, int32_t T, int32_t ntpr,
+                        void* stream) {
+    return dispatch_impl(ctx, d_x, d_scores, d_ids, d_counts, T, ntpr, stream, true);
+}
+
+int moe_topk_from_routing_map(moe_ctx* ctx, const uint8_t* d_routing_map, const float* d_probs,
+                              int32_t T, void* stream, int32_t** d_topk_ids_out,
+                              float** d_topk_scores_out, int32_t** d_n_experts_out) {
+    if (!ctx || !d_topk_ids_out || !d_topk_scores_out || !d_n_experts_out)
+        return MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > ctx->cfg.num_max_tokens_per_rank) return MOE_ERR_CAPACITY;
+    if (T > 0 && (!d_routing_map || !d_probs)) return MOE_ERR_INVALID_ARG;
+    moe::TopkFromMapArgs a;
+    a.map = d_routing_map;
+    a.probs = d_probs;
+    a.T = T;
+    a.E = ctx->cfg.num_experts;
+    a.K = ctx->cfg.topk;
+    a.ids = at<int32_t>(ctx, ctx->desc.map_ids);
+    a.scores = at<float>(ctx, ctx->desc.map_scores);
+    a.n_experts = at<int32_t>(ctx, ctx->desc.map_n_experts);
+    if (moe::launch_topk_from_map(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    *d_topk_ids_out = a.ids;
+    *d_topk_scores_out = a.scores;
+    *d_n_experts_out = a.n_experts;
     return MOE_OK;
 }
 
@@ -313,7 +354,9 @@ int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
     int64_t ntpr4 = 0;
     const int st = check_call(ctx, T, ntpr, &ntpr4);
     if (st != MOE_OK) return st;
-    if (T > 0 && (!d_y_expert || !d_row_map || !d_scores)) return MOE_ERR_INVALID_ARG;
+    // d_scores may be NULL: every weight is then 1 (the scores were applied
+    // by moe_dispatch_scaled, or the caller wants the plain sum).
+    if (T > 0 && (!d_y_expert || !d_row_map)) return MOE_ERR_INVALID_ARG;
     if (d_row_map == at<int32_t>(ctx, ctx->desc.row_map) &&
         (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4))
         return MOE_ERR_STATE;

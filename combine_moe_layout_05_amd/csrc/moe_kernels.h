@@ -80,6 +80,8 @@ struct DispatchArgs {
     int32_t segments;
     int32_t block_waves;    // wavefronts per workgroup, 1..16
     bool nontemporal;
+    bool scaled;            // x_e[r] = scores[t][k] * x[t] instead of a bit copy
+    bool bf16;              // element type (used when scaled)
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
@@ -114,5 +116,17 @@ struct CombineBackwardArgs {
     float* grad_s;          // [T][K]
 };
 hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t stream);
+
+struct TopkFromMapArgs {
+    const uint8_t* map;     // [T][E], nonzero = routed
+    const float* probs;     // [T][E]
+    int32_t T;
+    int32_t E;
+    int32_t K;
+    int32_t* ids;           // [T][K]
+    float* scores;          // [T][K]
+    int32_t* n_experts;     // [T]
+};
+hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 
 }  // namespace moe

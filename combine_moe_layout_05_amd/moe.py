@@ -106,6 +106,9 @@ class MoeDispatcher:
         self.s_e = self._view(d.s_e, d.max_rows, torch.float32)
         self.x_e = self._view(d.x_e, d.max_rows * D, dtype).view(d.max_rows, D)
         self.y = self._view(d.y, self.nmax4 * D, dtype).view(self.nmax4, D)
+        self.map_ids = self._view(d.map_ids, d.max_rows, torch.int32).view(self.nmax4, K)
+        self.map_scores = self._view(d.map_scores, d.max_rows, torch.float32).view(self.nmax4, K)
+        self.map_n_experts = self._view(d.map_n_experts, self.nmax4, torch.int32)
         if backward:
             self.g_e = self._view(d.g_e, d.max_rows * D, dtype).view(d.max_rows, D)
             self.g_s = self._view(d.g_s, d.max_rows, torch.float32).view(self.nmax4, K)
@@ -152,40 +155,79 @@ class MoeDispatcher:
                  *, num_tokens_per_rank: Optional[int] = None) -> Dispatched:
         """Permute x rows and scores into the expert-major buffers using the
         row map of the preceding layout() on the same ids."""
+        return self._dispatch(self._lib.moe_dispatch, "moe_dispatch", x_TD, topk_scores_TK,
+                              topk_expert_ids_TK, num_local_tokens_per_expert_E,
+                              num_tokens_per_rank)
+
+    def dispatch_scaled(self, x_TD: torch.Tensor, topk_scores_TK: torch.Tensor,
+                        topk_expert_ids_TK: torch.Tensor,
+                        num_local_tokens_per_expert_E: torch.Tensor, *,
+                        num_tokens_per_rank: Optional[int] = None) -> Dispatched:
+        """dispatch() with each copy scaled by its slot's score (one fp32
+        product, rounded); pair with combine(topk_scores_TK=None)."""
+        return self._dispatch(self._lib.moe_dispatch_scaled, "moe_dispatch_scaled", x_TD,
+                              topk_scores_TK, topk_expert_ids_TK,
+                              num_local_tokens_per_expert_E, num_tokens_per_rank)
+
+    def _dispatch(self, fn, what, x_TD, topk_scores_TK, topk_expert_ids_TK, counts,
+                  num_tokens_per_rank) -> Dispatched:
         x = self._dev(x_TD, "x_TD", self.dtype, self.hidden)
         T = x.shape[0]
         s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
         ids = self._dev(topk_expert_ids_TK, "topk_expert_ids_TK", torch.int32, self.topk)
         if s.shape[0] != T or ids.shape[0] != T:
             raise ValueError("x_TD, topk_scores_TK and topk_expert_ids_TK need the same T")
-        counts = num_local_tokens_per_expert_E
         ntpr = self._ntpr(T, num_tokens_per_rank)
-        L.check(self._lib.moe_dispatch(self._ctx, x.data_ptr(), s.data_ptr(), ids.data_ptr(),
-                                       counts.data_ptr(), T, ntpr, _stream(self.device)),
-                "moe_dispatch")
+        L.check(fn(self._ctx, x.data_ptr(), s.data_ptr(), ids.data_ptr(), counts.data_ptr(), T,
+                   ntpr, _stream(self.device)), what)
         rows = round_up4(ntpr) * self.topk
         return Dispatched(self.x_e[:rows], self.s_e[:rows])
 
-    def combine(self, y_expert: torch.Tensor, row_map: torch.Tensor, topk_scores_TK: torch.Tensor,
-                *, num_tokens_per_rank: Optional[int] = None) -> torch.Tensor:
+    def topk_from_routing_map(self, routing_map_TE: torch.Tensor, probs_TE: torch.Tensor):
+        """(ids [T, K], scores [T, K], n_experts [T]) views: the top-k form of
+        a boolean routing map with probabilities (experts in ascending order,
+        -1 / 0 past a token's experts)."""
+        m = routing_map_TE
+        if m.dtype == torch.bool:
+            m = m.view(torch.uint8)
+        m = self._dev(m, "routing_map_TE", torch.uint8, self.num_experts)
+        p = self._dev(probs_TE, "probs_TE", torch.float32, self.num_experts)
+        T = m.shape[0]
+        if p.shape[0] != T:
+            raise ValueError("routing_map_TE and probs_TE need the same T")
+        o_ids, o_s, o_n = C.c_void_p(), C.c_void_p(), C.c_void_p()
+        L.check(self._lib.moe_topk_from_routing_map(self._ctx, m.data_ptr(), p.data_ptr(), T,
+                                                    _stream(self.device), C.byref(o_ids),
+                                                    C.byref(o_s), C.byref(o_n)),
+                "moe_topk_from_routing_map")
+        return self.map_ids[:T], self.map_scores[:T], self.map_n_experts[:T]
+
+    def combine(self, y_expert: torch.Tensor, row_map: torch.Tensor,
+                topk_scores_TK: Optional[torch.Tensor], *,
+                num_tokens_per_rank: Optional[int] = None, T: Optional[int] = None) -> torch.Tensor:
         """Score-weighted sum of expert outputs back to token order; returns
-        y[:T] (a view of the persistent output buffer)."""
-        s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
-        T = s.shape[0]
+        y[:T] (a view of the persistent output buffer). topk_scores_TK=None
+        gives unit weights (then T is required)."""
+        if topk_scores_TK is None:
+            if T is None:
+                raise ValueError("T is required when topk_scores_TK is None")
+            s_ptr = 0
+        else:
+            s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
+            if T is not None and T != s.shape[0]:
+                raise ValueError("T differs from topk_scores_TK.shape[0]")
+            T = s.shape[0]
+            s_ptr = s.data_ptr()
         if y_expert.device != self.device or y_expert.dtype != self.dtype:
             raise TypeError("y_expert must match the dispatcher's device and dtype")
         if y_expert.dim() != 2 or y_expert.shape[1] != self.hidden or not y_expert.is_contiguous():
             raise ValueError(f"y_expert must be a contiguous [rows, {self.hidden}] tensor")
-        rm = row_map
-        if rm.device != self.device or rm.dtype != torch.int32 or not rm.is_contiguous():
-            raise ValueError("row_map must be a contiguous int32 tensor on the device")
-        if rm.dim() != 2 or rm.shape[1] != self.topk or rm.shape[0] < T:
-            raise ValueError(f"row_map must be [>= T, {self.topk}]")
+        rm = self._row_map(row_map, T)
         ntpr = self._ntpr(T, num_tokens_per_rank)
         if y_expert.shape[0] < round_up4(ntpr) * self.topk:
             raise ValueError("y_expert needs round_up4(num_tokens_per_rank) * topk rows")
         out = C.c_void_p()
-        L.check(self._lib.moe_combine(self._ctx, y_expert.data_ptr(), rm.data_ptr(), s.data_ptr(),
+        L.check(self._lib.moe_combine(self._ctx, y_expert.data_ptr(), rm.data_ptr(), s_ptr,
                                       T, ntpr, _stream(self.device), C.byref(out)),
                 "moe_combine")
         return self.y[:T]

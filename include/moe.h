@@ -100,6 +100,8 @@ typedef struct moe_config {
  *   y           dtype [nmax4][D]     combined output; rows [0,T) of a call
  *   block_hist  int32 [max_tiles][round_up4(E)] layout scratch (per-tile
  *                                    histograms)
+ *   map_ids, map_scores  int32 / f32 [nmax4][K]  top-k form of a routing map
+ *   map_n_experts        int32 [nmax4]          experts per routing-map row
  * With MOE_FLAG_BACKWARD (offsets are -1 without it):
  *   g_e         dtype [nmax4*K][D]   dL/dy_e from moe_combine_backward
  *   g_s         f32   [nmax4][K]     dL/dscores from moe_combine_backward
@@ -114,6 +116,7 @@ typedef struct moe_buffers_desc {
     int64_t tile_slots;    /* (t,k) slots per layout tile */
     int64_t counts, offsets, row_map, src_map, s_e, x_e, y;
     int64_t block_hist;
+    int64_t map_ids, map_scores, map_n_experts;
     int64_t g_e, g_s, g_x;
 } moe_buffers_desc;
 
@@ -169,6 +172,36 @@ int moe_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
                  const int32_t *d_topk_ids, const int32_t *d_counts, int32_t T,
                  int32_t num_tokens_per_rank, void *stream);
 
+/* Dispatch with the scores applied (the weighting moved from the combine to
+ * the dispatch; [NA] "Fix": the dispatcher's inputs are hidden states,
+ * routing map and probabilities). Same arguments, checks and rows as
+ * moe_dispatch, but
+ *   x_e[row_map[t][k]] = scores[t][k] * x[t]
+ * as one fp32 product rounded to the element type (bf16: to nearest even).
+ * s_e still receives the scores. Pair it with moe_combine(d_topk_scores =
+ * NULL) so the weights are not applied twice. */
+int moe_dispatch_scaled(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
+                        const int32_t *d_topk_ids, const int32_t *d_counts, int32_t T,
+                        int32_t num_tokens_per_rank, void *stream);
+
+/* Routing-map input format ([NA] "Fix": HybridEP's dispatcher takes a
+ * boolean routing map [T][E] and probabilities [T][E]; padded rows are
+ * all-False with zero probabilities). Writes the top-k form into the
+ * context: for t < T, slot k of token t is the k-th expert e, ascending, with
+ * d_routing_map[t][e] != 0 and score d_probs[t][e]; the remaining slots get
+ * id -1 and score 0 (no expert). n_experts[t] is the row's number of experts;
+ * a row with more than K keeps its K lowest (n_experts[t] > K reports it on
+ * the device, with no host round trip).
+ *   d_routing_map  uint8 [T][E] (torch.bool works), d_probs float32 [T][E]
+ *   *d_topk_ids_out, *d_topk_scores_out  receive map_ids / map_scores
+ *                  ([nmax4][K], rows [0,T) written), ready for moe_layout,
+ *                  moe_dispatch and moe_combine
+ *   *d_n_experts_out receives map_n_experts ([nmax4], rows [0,T))
+ * Requires 0 <= T <= num_max_tokens_per_rank (MOE_ERR_CAPACITY). */
+int moe_topk_from_routing_map(moe_ctx *ctx, const uint8_t *d_routing_map, const float *d_probs,
+                              int32_t T, void *stream, int32_t **d_topk_ids_out,
+                              float **d_topk_scores_out, int32_t **d_n_experts_out);
+
 /* Combine ([NA] "Fix" and "Testing"). For t < T:
  *   y[t] = sum over k = 0..K-1 with d_row_map[t][k] >= 0 of
  *          scores[t][k] * y_expert[d_row_map[t][k]]
@@ -183,7 +216,8 @@ int moe_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
  *   d_row_map   [>= T][K] row map, normally the context's; when it is the
  *               context's, T and num_tokens_per_rank must match the most
  *               recent moe_layout (MOE_ERR_STATE otherwise)
- *   d_topk_scores [T][K] float32
+ *   d_topk_scores [T][K] float32, or NULL for unit weights (after
+ *               moe_dispatch_scaled, which already applied the scores)
  *   *d_y_out    receives the device address of y ([nmax4][D], rows [0,T)
  *               valid until the next combine on this context).
  * Rows of d_row_map outside [0, round_up4(num_tokens_per_rank) * K) are

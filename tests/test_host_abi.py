@@ -102,7 +102,8 @@ def test_workspace_carve_up(lib, nmax, D, E, K, dtype, flags):
     assert d.nmax4 == n4 and d.max_rows == n4 * K and d.row_bytes == D * eb
     sizes = {"counts": E * 4, "offsets": (E + 1) * 4, "row_map": n4 * K * 4,
              "src_map": n4 * K * 4, "s_e": n4 * K * 4, "x_e": n4 * K * D * eb,
-             "y": n4 * D * eb, "block_hist": d.max_tiles * oracle.round_up4(E) * 4}
+             "y": n4 * D * eb, "block_hist": d.max_tiles * oracle.round_up4(E) * 4,
+             "map_ids": n4 * K * 4, "map_scores": n4 * K * 4, "map_n_experts": n4 * 4}
     if flags & L.MOE_FLAG_BACKWARD:
         sizes.update(g_e=n4 * K * D * eb, g_s=n4 * K * 4, g_x=n4 * D * eb)
     else:
@@ -186,6 +187,25 @@ def test_backward_calls_need_the_flag_and_a_matching_layout(lib):
                                     C.byref(out_s)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(ctx, None, p, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(ctx, p, p, 5, 4097, None, C.byref(out_x)) == L.MOE_ERR_CAPACITY
+    lib.moe_destroy(ctx)
+
+
+def test_variant_calls_reject_bad_arguments(lib):
+    ctx, d, _ = _ctx(lib, _cfg(4096, 2048, 128, 8, L.MOE_BF16))
+    p = 1 << 41
+    o1, o2, o3 = C.c_void_p(), C.c_void_p(), C.c_void_p()
+    assert lib.moe_topk_from_routing_map(ctx, p, p, 4097, None, C.byref(o1), C.byref(o2),
+                                         C.byref(o3)) == L.MOE_ERR_CAPACITY
+    assert lib.moe_topk_from_routing_map(ctx, p, p, -1, None, C.byref(o1), C.byref(o2),
+                                         C.byref(o3)) == L.MOE_ERR_CAPACITY
+    assert lib.moe_topk_from_routing_map(ctx, None, p, 5, None, C.byref(o1), C.byref(o2),
+                                         C.byref(o3)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_topk_from_routing_map(ctx, p, p, 5, None, None, C.byref(o2),
+                                         C.byref(o3)) == L.MOE_ERR_INVALID_ARG
+    counts = (1 << 40) + d.counts
+    assert lib.moe_dispatch_scaled(ctx, p, p, p, counts, 5, 8, None) == L.MOE_ERR_STATE
+    assert lib.moe_dispatch_scaled(ctx, p, p, p, counts + 4, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_scaled(ctx, p, None, p, counts, 5, 8, None) == L.MOE_ERR_INVALID_ARG
     lib.moe_destroy(ctx)
 
 
