@@ -18,6 +18,19 @@ def note(msg: str) -> None:
     sys.stdout.flush()
 
 
+def sync_or_fail(timeout_s: float = 30.0, stream=None) -> None:
+    """Wait for the stream by polling it against a deadline, so a hang turns
+    into a test failure instead of a blocked process."""
+    import time
+    s = stream if stream is not None else torch.cuda.current_stream(DEV)
+    deadline = time.monotonic() + timeout_s
+    while not s.query():
+        if time.monotonic() > deadline:
+            raise TimeoutError(f"GPU work did not finish within {timeout_s} s")
+        time.sleep(0.0005)
+    torch.cuda.synchronize()
+
+
 def x_to_dev(x: np.ndarray) -> torch.Tensor:
     if x.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)

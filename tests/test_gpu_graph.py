@@ -16,7 +16,7 @@ import workloads
 from combine_moe_layout_05_amd import MoeDispatcher
 
 from gpu_util import (DEV, ORACLE_THREADS, assert_combine_within_bar, f32_dev, i32_dev,
-                      note, x_to_dev, x_to_np)
+                      note, sync_or_fail, x_to_dev, x_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,8 +101,13 @@ def test_graph_replays_with_fresh_routing(cap, chunk):
         T = b["T"]
         note(f"graph replay {i} T={T}")
         cap.load(b)
+        if i % 10 == 7:
+            # poison every persistent buffer between replays: the replay must
+            # rebuild everything it reads (no state carries over)
+            cap.disp.workspace.fill_(0xFF)
+            cap.y_e.fill_(0xFF)
         cap.graph.replay()
-        torch.cuda.synchronize()
+        sync_or_fail()
         y = x_to_np(cap.y)
         o = _oracle(b, T, T)
         np.testing.assert_array_equal(cap.disp.counts.cpu().numpy(), o["counts"])
@@ -185,7 +190,7 @@ def test_graph_buckets_with_different_capacities_share_one_context():
         st["gy"][T:].zero_()
         note(f"bucket {n} replay {i} T={T}")
         g.replay()
-        torch.cuda.synchronize()
+        sync_or_fail()
         o = oracle.run_pipeline(b["x"], b["ids"], b["scores"], T, T, E, K, nthreads=ORACLE_THREADS)
         assert np.array_equal(x_to_np(y)[:T], o["y"])
         assert (x_to_np(y)[T:] == 0).all()
