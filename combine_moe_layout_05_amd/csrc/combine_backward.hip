@@ -12,14 +12,17 @@
 //
 // One workgroup per token, W = ceil(chunks/64) wavefronts (at most 16): each
 // lane owns 16-byte chunks lane + 64*wave + 64*W*i of the row, so the
-// workgroup reads dL/dy[t] once, reads the K expert rows (streaming loads),
-// writes the K scaled rows, and reduces the K dot products: in element order
-// within a lane, then a fixed butterfly over the 64 lanes, then the
-// wavefronts in order. The reduction order is fixed, so results are
+// workgroup reads dL/dy[t] once, reads the K expert rows (streaming loads,
+// all issued before use; a no-expert slot reads the token's first valid row
+// and skips it), writes the K scaled rows, and reduces the K dot products:
+// in element order within a lane, then a fixed butterfly over the 64 lanes,
+// then the wavefronts in order. The reduction order is fixed, so results are
 // deterministic; it differs from plain left-to-right order, which stays
 // within the fp32 summation error bound of the dot product.
 #include "moe_kernels.h"
 #include "moe_lanes.h"
+
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -59,19 +62,39 @@ void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restri
     float dot[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) dot[k] = 0.0f;
-    const v4i* g = grad_y + t * chunks;
-    for (int32_t c = wave * 64 + lane; c < chunks; c += waves * 64) {
-        const v4i gv = g[c];
-        v4i yv[K];
+    int32_t fallback = -1;
+    bool all_valid = true;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (fallback < 0 && row[k] >= 0) fallback = row[k];
+        all_valid = all_valid && row[k] >= 0;
+    }
+    if (fallback >= 0) {
+        // No-expert slots read the token's first valid row instead (written,
+        // finite) and skip it, so every load is unconditional.
+        const v4i* src[K];
 #pragma unroll
         for (int k = 0; k < K; ++k)
-            if (row[k] >= 0) yv[k] = fetch<true>(y_e + int64_t(row[k]) * chunks + c);
+            src[k] = y_e + int64_t(row[k] >= 0 ? row[k] : fallback) * chunks;
+        const v4i* g = grad_y + t * chunks;
+        auto pass = [&](auto every) {
+            for (int32_t c = wave * 64 + lane; c < chunks; c += waves * 64) {
+                const v4i gv = g[c];
+                v4i yv[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (row[k] < 0) continue;
-            grad_y_e[int64_t(row[k]) * chunks + c] = L::scale(s[k], gv);
-            dot[k] = L::dot_into(dot[k], gv, yv[k]);
-        }
+                for (int k = 0; k < K; ++k) yv[k] = fetch<true>(src[k] + c);
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    if (!decltype(every)::value && row[k] < 0) continue;
+                    grad_y_e[int64_t(row[k]) * chunks + c] = L::scale(s[k], gv);
+                    dot[k] = L::dot_into(dot[k], gv, yv[k]);
+                }
+            }
+        };
+        if (all_valid)
+            pass(std::true_type{});
+        else
+            pass(std::false_type{});
     }
 
     // Lanes, then wavefronts, in a fixed order.

@@ -14,7 +14,8 @@
 //   src_map[row]   = t*K+k
 //
 // Two launches, no atomics on global memory and no host round trip:
-//   1. count: each workgroup histograms a 1024-slot tile into LDS and writes
+//   1. count: each workgroup histograms a tile of 512 or 1024 slots (chosen
+//      per call by the slot count) into LDS and writes
 //      its row of block_hist[tile][e].
 //   2. rank: each workgroup first turns the tile histograms into the global
 //      offsets (sum over all tiles, exclusive scan over experts) and its own
@@ -57,6 +58,7 @@ __device__ __forceinline__ int32_t slot_expert(const int32_t* __restrict__ ids,
 
 // Histogram rows are padded to E4 = round_up(E, 4) entries (zeros past E) so
 // they can be read as 16-byte vectors.
+template <int R>
 __global__ __launch_bounds__(kLayoutThreads)
 void layout_count_kernel(const int32_t* __restrict__ ids, int64_t nvalid,
                          int32_t E, int32_t E4, int bits, int32_t* __restrict__ block_hist) {
@@ -67,15 +69,15 @@ void layout_count_kernel(const int32_t* __restrict__ ids, int64_t nvalid,
     for (int e = tid; e < E4; e += kLayoutThreads) hist[e] = 0;
     __syncthreads();
 
-    const int64_t base = int64_t(blockIdx.x) * kLayoutTile + wave * (64 * kLayoutSlotsPerLane);
-    int32_t ex[kLayoutSlotsPerLane];
+    const int64_t base = int64_t(blockIdx.x) * (kLayoutThreads * R) + wave * (64 * R);
+    int32_t ex[R];
 #pragma unroll
-    for (int j = 0; j < kLayoutSlotsPerLane; ++j)
+    for (int j = 0; j < R; ++j)
         ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
 
     const uint64_t below = lanes_below();
 #pragma unroll
-    for (int j = 0; j < kLayoutSlotsPerLane; ++j) {
+    for (int j = 0; j < R; ++j) {
         const bool valid = ex[j] >= 0;
         const uint64_t peers = peer_mask(ex[j], valid, bits);
         if (valid && (peers & below) == 0) atomicAdd(&hist[ex[j]], __popcll(peers));
@@ -91,6 +93,7 @@ constexpr int kExpertsPerThread = kMaxExperts / kLayoutThreads;
 constexpr int kMaxSlices = 16;
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
+template <int R>
 __global__ __launch_bounds__(kLayoutThreads)
 void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t nslots,
                         int32_t E, int32_t E4, int bits, int32_t tiles,
@@ -183,11 +186,11 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
         offsets[E] = total;
     }
 
-    const int64_t base = int64_t(blockIdx.x) * kLayoutTile + wave * (64 * kLayoutSlotsPerLane);
-    int32_t ex[kLayoutSlotsPerLane];
-    int32_t local[kLayoutSlotsPerLane];
+    const int64_t base = int64_t(blockIdx.x) * (kLayoutThreads * R) + wave * (64 * R);
+    int32_t ex[R];
+    int32_t local[R];
 #pragma unroll
-    for (int j = 0; j < kLayoutSlotsPerLane; ++j)
+    for (int j = 0; j < R; ++j)
         ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
 
     // Rank within this wavefront's run, chunk by chunk in slot order. All
@@ -196,7 +199,7 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
     int32_t* mine = wave_hist[wave];
     const uint64_t below = lanes_below();
 #pragma unroll
-    for (int j = 0; j < kLayoutSlotsPerLane; ++j) {
+    for (int j = 0; j < R; ++j) {
         const bool valid = ex[j] >= 0;
         const uint64_t peers = peer_mask(ex[j], valid, bits);
         const int32_t before = valid ? mine[ex[j]] : 0;
@@ -219,7 +222,7 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
     __syncthreads();
 
 #pragma unroll
-    for (int j = 0; j < kLayoutSlotsPerLane; ++j) {
+    for (int j = 0; j < R; ++j) {
         const int64_t i = base + j * 64 + lane;
         if (i >= nslots) continue;
         if (ex[j] >= 0) {
@@ -234,14 +237,13 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
     }
 }
 
-}  // namespace
-
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    const int64_t tiles = layout_tiles(a.nslots);
+template <int R>
+hipError_t launch_r(const LayoutArgs& a, hipStream_t stream) {
+    const int64_t tiles = layout_tiles(a.nslots, R);
     const int bits = expert_bits(a.E);
     const int32_t E4 = padded_experts(a.E);
     if (tiles > 0) {
-        hipLaunchKernelGGL(layout_count_kernel, dim3(static_cast<uint32_t>(tiles)),
+        hipLaunchKernelGGL(layout_count_kernel<R>, dim3(static_cast<uint32_t>(tiles)),
                            dim3(kLayoutThreads), 0, stream, a.ids, a.nvalid, a.E, E4, bits,
                            a.block_hist);
         const hipError_t err = hipGetLastError();
@@ -250,10 +252,18 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     // At least one workgroup, so counts and offsets are written even for an
     // empty capacity.
     const uint32_t grid = static_cast<uint32_t>(tiles > 0 ? tiles : 1);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(grid), dim3(kLayoutThreads), 0, stream, a.ids,
+    hipLaunchKernelGGL(layout_rank_kernel<R>, dim3(grid), dim3(kLayoutThreads), 0, stream, a.ids,
                        a.nvalid, a.nslots, a.E, E4, bits, static_cast<int32_t>(tiles), a.block_hist,
                        a.counts, a.offsets, a.row_map, a.src_map);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+    return layout_slots_per_lane(a.nslots) == kLayoutMinSlotsPerLane
+               ? launch_r<kLayoutMinSlotsPerLane>(a, stream)
+               : launch_r<kLayoutMaxSlotsPerLane>(a, stream);
 }
 
 }  // namespace moe

@@ -8,13 +8,21 @@
 
 namespace moe {
 
-// Layout: one workgroup of 4 wavefronts sorts a tile of 1024 (t,k) slots;
-// each lane holds 4 slots, one per 64-slot chunk of its wavefront's
-// 256-slot run.
+// Layout: one workgroup of 4 wavefronts sorts a tile of 256*R (t,k) slots;
+// each lane holds R slots, one per 64-slot chunk of its wavefront's run.
+// R is chosen per call: 2 (512-slot tiles) up to kLayoutSmallSlots slots, 4
+// (1024-slot tiles) above (measured on MI355X: more, smaller tiles win while
+// the tile count is small; past that the per-tile offset sums dominate).
 constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / 64;
-constexpr int kLayoutSlotsPerLane = 4;
-constexpr int kLayoutTile = kLayoutThreads * kLayoutSlotsPerLane;
+constexpr int kLayoutMinSlotsPerLane = 2;
+constexpr int kLayoutMaxSlotsPerLane = 4;
+constexpr int64_t kLayoutSmallSlots = 65536;
+// The largest tile count any call can use: the smallest tile.
+constexpr int kLayoutTile = kLayoutThreads * kLayoutMinSlotsPerLane;
+inline int layout_slots_per_lane(int64_t slots) {
+    return slots <= kLayoutSmallSlots ? kLayoutMinSlotsPerLane : kLayoutMaxSlotsPerLane;
+}
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
 
@@ -30,9 +38,14 @@ constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;
 
 static_assert(kMaxExperts % kLayoutThreads == 0, "experts split evenly over layout threads");
 
-// Number of layout tiles covering n slots.
+// Number of layout tiles covering n slots with R slots per lane; without R,
+// the most any call can use.
+inline int64_t layout_tiles(int64_t slots, int slots_per_lane) {
+    const int64_t tile = int64_t(kLayoutThreads) * slots_per_lane;
+    return (slots + tile - 1) / tile;
+}
 inline int64_t layout_tiles(int64_t slots) {
-    return (slots + kLayoutTile - 1) / kLayoutTile;
+    return layout_tiles(slots, kLayoutMinSlotsPerLane);
 }
 
 // Experts rounded up to a multiple of 4: the row stride of the per-tile

@@ -112,8 +112,8 @@ typedef struct moe_buffers_desc {
     int64_t nmax4;
     int64_t max_rows;      /* nmax4 * K */
     int64_t row_bytes;     /* D * element size */
-    int64_t max_tiles;     /* layout tiles at full capacity */
-    int64_t tile_slots;    /* (t,k) slots per layout tile */
+    int64_t max_tiles;     /* layout tiles at full capacity (smallest tile) */
+    int64_t tile_slots;    /* (t,k) slots of the smallest layout tile */
     int64_t counts, offsets, row_map, src_map, s_e, x_e, y;
     int64_t block_hist;
     int64_t map_ids, map_scores, map_n_experts;
