@@ -8,3 +8,4 @@ from .moe import (  # noqa: F401
     num_max_tokens_pretrain, round_up4, validate_num_max,
 )
 from ._lib import MoeError, load  # noqa: F401
+from .autograd import MoeTokenDispatcher  # noqa: F401
