@@ -12,4 +12,5 @@ from .oracle import (  # noqa: F401
     num_max_infer, validate_num_max, check_capacity, layout, dispatch,
     dispatch_rows, combine, combine_tokens, f32_to_bf16, run_pipeline,
     combine_backward, dispatch_backward, topk_from_routing_map, dispatch_scaled,
+    grouped_gemm, grouped_gemm_at, f64_to_bf16, run_layer,
 )

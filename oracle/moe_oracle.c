@@ -389,3 +389,91 @@ void orc_dispatch_scaled(const void *x, int dtype, int64_t D, const float *score
             orc_store_elem(x_e, dtype, r * D + d, s * orc_load_elem(x, dtype, t * D + d));
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Expert step between dispatch and combine ([UC] "Tests": layout, dispatch,
+ * expert and combine run as one captured graph, checked against an analytic
+ * oracle; "Internode" item 2: the expert step takes its per-expert row counts
+ * from device memory). Reading: each expert is one linear map, its weight
+ * stored as N rows of Kd elements (a linear layer's [out][in] layout).     */
+
+static double orc_bf16_to_f64(uint16_t h)
+{
+    return (double)orc_bf16_to_f32(h);
+}
+
+/* Dot product of row r of x_e with row n of expert e's weight, in fp64. */
+static double orc_expert_dot(const uint16_t *x_e, const uint16_t *w, int32_t e,
+                             int64_t Kd, int64_t N, int64_t r, int64_t n)
+{
+    const uint16_t *xr = x_e + r * Kd;
+    const uint16_t *wr = w + ((int64_t)e * N + n) * Kd;
+    double acc = 0.0;
+    for (int64_t d = 0; d < Kd; ++d)
+        acc += orc_bf16_to_f64(xr[d]) * orc_bf16_to_f64(wr[d]);
+    return acc;
+}
+
+/*
+ * x_e [rows][Kd] bf16, w [E][N][Kd] bf16, offsets [E+1] (exclusive prefix sum
+ * of the per-expert row counts). For every expert e and every row r with
+ * offsets[e] <= r < offsets[e+1]:
+ *     out[r][n] = sum over d of x_e[r][d] * w[e][n][d]      (fp64)
+ * Rows outside every segment are not written.
+ */
+void orc_grouped_gemm(const uint16_t *x_e, const uint16_t *w, const int32_t *offsets,
+                      int32_t E, int64_t Kd, int64_t N, double *out, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t r0 = offsets[e], r1 = offsets[e + 1];
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t n = 0; n < N; ++n)
+                out[r * N + n] = orc_expert_dot(x_e, w, e, Kd, N, r, n);
+    }
+}
+
+/* The same values at count chosen positions (rows[i], cols[i]); a row that
+ * lies in no segment gives NaN. For outputs too large to form whole. */
+void orc_grouped_gemm_at(const uint16_t *x_e, const uint16_t *w, const int32_t *offsets,
+                         int32_t E, int64_t Kd, int64_t N, const int64_t *rows,
+                         const int64_t *cols, int64_t count, double *out, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int32_t owner = -1;
+        for (int32_t e = 0; e < E; ++e)
+            if (offsets[e] <= rows[i] && rows[i] < offsets[e + 1]) owner = e;
+        out[i] = owner < 0 ? NAN : orc_expert_dot(x_e, w, owner, Kd, N, rows[i], cols[i]);
+    }
+}
+
+/* fp64 to bf16 bits in one rounding (nearest, ties to even; the detour
+ * through fp32 would round twice). NaN becomes 0x7FC0; magnitudes that
+ * round past the largest finite bf16 become infinity. */
+uint16_t orc_f64_to_bf16(double v)
+{
+    if (isnan(v)) return 0x7FC0;
+    double a = fabs(v), r;
+    if (a == 0.0 || isinf(a)) {
+        r = a;
+    } else {
+        int ex;
+        frexp(a, &ex);                  /* a = m * 2^ex, 0.5 <= m < 1 */
+        int qe = ex - 8;                /* 8 significant bits */
+        if (qe < -133) qe = -133;       /* spacing of bf16 subnormals */
+        r = ldexp(nearbyint(ldexp(a, -qe)), qe);
+        if (r >= 0x1p128) r = INFINITY;
+    }
+    float f = (float)copysign(r, v);    /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+void orc_f64_to_bf16_n(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(v[i]);
+}

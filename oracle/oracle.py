@@ -70,6 +70,12 @@ def _load():
         L.orc_topk_from_routing_map.restype = None
         L.orc_dispatch_scaled.argtypes = [vp, C.c_int, i64, vp, i32, vp, i64, vp, C.c_int]
         L.orc_dispatch_scaled.restype = None
+        L.orc_grouped_gemm.argtypes = [vp, vp, vp, i32, i64, i64, vp, C.c_int]
+        L.orc_grouped_gemm.restype = None
+        L.orc_grouped_gemm_at.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, i64, vp, C.c_int]
+        L.orc_grouped_gemm_at.restype = None
+        L.orc_f64_to_bf16_n.argtypes = [vp, i64, vp]
+        L.orc_f64_to_bf16_n.restype = None
         _lib = L
         return L
 
@@ -281,3 +287,68 @@ def dispatch_scaled(x: np.ndarray, scores: np.ndarray, K: int, src: np.ndarray,
         L.orc_dispatch_scaled(_ptr(x), _dtype_code(x), D, _ptr(scores), K, _ptr(src), src.size,
                               _ptr(x_e), nthreads)
     return x_e
+
+
+def _gemm_args(x_e, w, offsets):
+    x_e = np.ascontiguousarray(x_e)
+    w = np.ascontiguousarray(w)
+    if x_e.dtype != np.uint16 or w.dtype != np.uint16:
+        raise TypeError("the expert step takes bf16 bits (uint16) for x_e and w")
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E, N, Kd = w.shape
+    if offsets.shape != (E + 1,) or x_e.shape[1] != Kd:
+        raise ValueError("shapes: x_e [rows, Kd], w [E, N, Kd], offsets [E+1]")
+    if offsets[0] < 0 or np.any(np.diff(offsets) < 0) or offsets[-1] > x_e.shape[0]:
+        raise ValueError("offsets must be a non-decreasing prefix sum within x_e's rows")
+    return x_e, w, offsets, E, N, Kd
+
+
+def grouped_gemm(x_e: np.ndarray, w: np.ndarray, offsets: np.ndarray,
+                 nthreads: int = 1) -> np.ndarray:
+    """out [rows, N] float64: row r of expert e's segment is x_e[r] @ w[e].T
+    (w [E, N, Kd] bf16 bits); rows outside every segment stay NaN."""
+    L = _load()
+    x_e, w, offsets, E, N, Kd = _gemm_args(x_e, w, offsets)
+    out = np.full((x_e.shape[0], N), np.nan)
+    if out.size and offsets[-1] > 0:
+        L.orc_grouped_gemm(_ptr(x_e), _ptr(w), _ptr(offsets), E, Kd, N, _ptr(out), nthreads)
+    return out
+
+
+def grouped_gemm_at(x_e: np.ndarray, w: np.ndarray, offsets: np.ndarray, rows, cols,
+                    nthreads: int = 1) -> np.ndarray:
+    """The grouped_gemm values at positions (rows[i], cols[i]) only."""
+    L = _load()
+    x_e, w, offsets, E, N, Kd = _gemm_args(x_e, w, offsets)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape or np.any(cols < 0) or np.any(cols >= N):
+        raise ValueError("rows and cols: same shape, cols within [0, N)")
+    out = np.empty(rows.shape, np.float64)
+    if rows.size:
+        L.orc_grouped_gemm_at(_ptr(x_e), _ptr(w), _ptr(offsets), E, Kd, N, _ptr(rows),
+                              _ptr(cols), rows.size, _ptr(out), nthreads)
+    return out
+
+
+def f64_to_bf16(values) -> np.ndarray:
+    """Elementwise oracle rounding of float64 values to bf16 bits (one rounding)."""
+    L = _load()
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    if v.size:
+        L.orc_f64_to_bf16_n(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def run_layer(x: np.ndarray, ids: np.ndarray, scores: np.ndarray, w: np.ndarray, T: int,
+              ntpr: int, E: int, K: int, nthreads: int = 1) -> dict:
+    """Layout, dispatch, the expert step (w [E, D, D] bf16 bits; its output
+    rounded once to bf16) and combine of tokens [0,T)."""
+    lay = layout(ids[:T], T, ntpr, E, K)
+    x_e, s_e = dispatch(x[:T], scores[:T], K, lay["src"], nthreads)
+    h = grouped_gemm(x_e, w, lay["offsets"], nthreads)
+    y_e = f64_to_bf16(h)
+    y = combine(y_e, lay["row_map"], scores[:T], T, K, nthreads)
+    lay.update(x_e=x_e, s_e=s_e, h=h, y_e=y_e, y=y)
+    return lay
