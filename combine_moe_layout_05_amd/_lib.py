@@ -67,6 +67,7 @@ SIGNATURES = {
     "moe_combine_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp),
                                     C.POINTER(_vp)]),
     "moe_dispatch_backward": (_int, [_vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
+    "moe_grouped_gemm": (_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _i32, _vp]),
     "moe_set_tuning": (_int, [_vp, C.POINTER(MoeTuning)]),
     "moe_get_tuning": (_int, [_vp, C.POINTER(MoeTuning)]),
     "moe_ceil_div": (_i64, [_i64, _i64]),

@@ -14,6 +14,7 @@
 // in-flight work: counts and the total stay on the device.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -440,6 +441,45 @@ int moe_dispatch_backward(moe_ctx* ctx, const void* d_grad_x_expert, const int32
     if (moe::launch_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     *d_grad_x_out = a.y;
+    return MOE_OK;
+}
+
+
+int moe_grouped_gemm(const void* d_x_expert, const void* d_weights, const int32_t* d_offsets,
+                     int32_t num_experts, int64_t max_rows, int32_t k_in, int32_t n_out,
+                     void* d_out, int32_t row_tile, void* stream) {
+    if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+    if (max_rows < 0 || max_rows > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (k_in < 8 || k_in % 8 != 0 || n_out < 8 || n_out % 8 != 0) return MOE_ERR_INVALID_ARG;
+    if (row_tile != 0 && row_tile != moe::kGemmRowTileSmall && row_tile != moe::kGemmRowTileLarge)
+        return MOE_ERR_INVALID_ARG;
+    if (max_rows == 0) return MOE_OK;
+    if (!d_x_expert || !d_weights || !d_offsets || !d_out) return MOE_ERR_INVALID_ARG;
+    auto misaligned = [](const void* p, uintptr_t a) {
+        return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+    };
+    if (misaligned(d_x_expert, 16) || misaligned(d_weights, 16) || misaligned(d_out, 16) ||
+        misaligned(d_offsets, 4))
+        return MOE_ERR_INVALID_ARG;
+    // Automatic tile: 128 rows once the average expert could fill two such
+    // tiles at full capacity, else 64 (less padding for small segments).
+    if (row_tile == 0)
+        row_tile = max_rows >= int64_t(2) * moe::kGemmRowTileLarge * num_experts
+                       ? moe::kGemmRowTileLarge : moe::kGemmRowTileSmall;
+    if (moe::grouped_gemm_grid(max_rows, num_experts, n_out, row_tile) > INT32_MAX)
+        return MOE_ERR_INVALID_ARG;
+    moe::GroupedGemmArgs a;
+    a.x_e = d_x_expert;
+    a.w = d_weights;
+    a.offsets = d_offsets;
+    a.E = num_experts;
+    a.max_rows = max_rows;
+    a.Kd = k_in;
+    a.N = n_out;
+    a.row_tile = row_tile;
+    a.out = d_out;
+    if (moe::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -142,4 +142,27 @@ struct TopkFromMapArgs {
 };
 hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 
+// Expert step (grouped GEMM): workgroups of the launch for max_rows rows,
+// E experts, N output features and row tiles of row_tile rows: every
+// (feature tile of 128, row tile) pair the worst routing can need.
+inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile) {
+    const int64_t ftiles = (int64_t(N) + 127) / 128;
+    return ftiles * ((max_rows + row_tile - 1) / row_tile + E);
+}
+constexpr int kGemmRowTileSmall = 64;
+constexpr int kGemmRowTileLarge = 128;
+
+struct GroupedGemmArgs {
+    const void* x_e;        // [max_rows][Kd] bf16
+    const void* w;          // [E][N][Kd] bf16
+    const int32_t* offsets; // [E+1], device
+    int32_t E;
+    int64_t max_rows;       // <= INT32_MAX
+    int32_t Kd;             // multiple of 8
+    int32_t N;              // multiple of 8
+    int32_t row_tile;       // kGemmRowTileSmall or kGemmRowTileLarge
+    void* out;              // [max_rows][N] bf16
+};
+hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream);
+
 }  // namespace moe

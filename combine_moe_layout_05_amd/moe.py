@@ -60,6 +60,41 @@ def validate_num_max(configured: int, derived: int) -> None:
     L.check(L.load().moe_validate_num_max(configured, derived), "validate_num_max")
 
 
+def grouped_gemm(x_expert: torch.Tensor, weights: torch.Tensor, offsets: torch.Tensor,
+                 out: Optional[torch.Tensor] = None, *, row_tile: int = 0) -> torch.Tensor:
+    """Expert step between dispatch and combine (moe_grouped_gemm): for each
+    expert e, rows r in [offsets[e], offsets[e+1]) get
+    out[r] = x_expert[r] @ weights[e].T (fp32 accumulation, one rounding to
+    bf16). offsets stays on the device (e.g. Layout.offsets); rows outside
+    every segment keep what `out` held.
+
+    x_expert bf16 [R, k_in]; weights bf16 [E, n_out, k_in]; offsets int32
+    [E+1]; out bf16 [R, n_out] (allocated with torch.empty if None)."""
+    dev = x_expert.device
+    for name, t, dt, dim in (("x_expert", x_expert, torch.bfloat16, 2),
+                             ("weights", weights, torch.bfloat16, 3),
+                             ("offsets", offsets, torch.int32, 1)):
+        if t.device != dev:
+            raise ValueError(f"{name} must be on {dev}, got {t.device}")
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.dim() != dim or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dim}-d tensor")
+    E, n_out, k_in = weights.shape
+    R = x_expert.shape[0]
+    if x_expert.shape[1] != k_in or offsets.shape[0] != E + 1:
+        raise ValueError("shapes: x_expert [R, k_in], weights [E, n_out, k_in], offsets [E+1]")
+    if out is None:
+        out = torch.empty((R, n_out), dtype=torch.bfloat16, device=dev)
+    elif (out.device != dev or out.dtype != torch.bfloat16 or tuple(out.shape) != (R, n_out)
+          or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous bf16 [{R}, {n_out}] tensor on {dev}")
+    L.check(L.load().moe_grouped_gemm(x_expert.data_ptr(), weights.data_ptr(), offsets.data_ptr(),
+                                      E, R, k_in, n_out, out.data_ptr(), int(row_tile),
+                                      _stream(dev)), "moe_grouped_gemm")
+    return out
+
+
 class MoeDispatcher:
     """One persistent workspace for MoE token layout, dispatch and combine.
 

@@ -261,6 +261,40 @@ int moe_dispatch_backward(moe_ctx *ctx, const void *d_grad_x_expert, const int32
                           int32_t T, int32_t num_tokens_per_rank, void *stream,
                           void **d_grad_x_out);
 
+/* Expert step between dispatch and combine ([UC] "Tests": layout, dispatch,
+ * expert and combine captured in one graph; "Internode" item 2: the expert
+ * step takes its per-expert row counts from device memory, with no host
+ * handshake). Each expert applies one linear map to its segment of the
+ * expert-major rows (a grouped GEMM): for every e and every row r with
+ * offsets[e] <= r < offsets[e+1],
+ *   out[r][n] = sum over d < k_in of x_expert[r][d] * weights[e][n][d]
+ * bf16 inputs, fp32 accumulation (matrix cores; summation order not
+ * specified), rounded once to bf16 (nearest even). Rows outside every
+ * segment are not written. Needs no context and no workspace.
+ *   d_x_expert  bf16 [max_rows][k_in]  (x_e of moe_dispatch when k_in = hidden)
+ *   d_weights   bf16 [num_experts][n_out][k_in]  (expert e's weight as n_out
+ *               rows of k_in: a linear layer's [out][in] layout)
+ *   d_offsets   int32 [num_experts + 1] in device memory, read only by the
+ *               kernel: a non-decreasing prefix sum from 0 with
+ *               offsets[num_experts] <= max_rows (the context's offsets
+ *               after moe_layout satisfy this with max_rows =
+ *               round_up4(num_tokens_per_rank) * K). Other values cannot
+ *               make the kernel access memory outside the three buffers
+ *               (segments are clamped to [0, max_rows)), but the rows
+ *               written are then unspecified.
+ *   max_rows    rows the launch covers (0 <= max_rows <= INT32_MAX;
+ *               0 enqueues nothing)
+ *   k_in, n_out multiples of 8, >= 8
+ *   d_out       bf16 [max_rows][n_out]; must not overlap the inputs
+ *   row_tile    rows per tile: 64, 128, or 0 for the library's choice
+ *               (results do not depend on it)
+ * d_x_expert, d_weights and d_out must be 16-byte aligned, d_offsets
+ * 4-byte aligned. 1 <= num_experts <= MOE_MAX_EXPERTS. Violations:
+ * MOE_ERR_INVALID_ARG. */
+int moe_grouped_gemm(const void *d_x_expert, const void *d_weights, const int32_t *d_offsets,
+                     int32_t num_experts, int64_t max_rows, int32_t k_in, int32_t n_out,
+                     void *d_out, int32_t row_tile, void *stream);
+
 /* Launch shape tuning (optional). Each token row is split into `segments`
  * wavefront work items (1..16) and `block_waves` wavefronts (1..16) form a
  * workgroup; 0 keeps the current value. A nonzero *_nontemporal marks

@@ -209,6 +209,27 @@ def test_variant_calls_reject_bad_arguments(lib):
     lib.moe_destroy(ctx)
 
 
+def test_grouped_gemm_rejects_bad_arguments(lib):
+    p = 1 << 41                                   # 16-byte aligned, never dereferenced
+    ok = dict(x=p, w=p, off=p, E=256, rows=32768, k=7168, n=4096, out=p, tile=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_grouped_gemm(a["x"], a["w"], a["off"], a["E"], a["rows"], a["k"], a["n"],
+                                    a["out"], a["tile"], None)
+
+    bad = L.MOE_ERR_INVALID_ARG
+    for kw in (dict(E=0), dict(E=1025), dict(rows=-1), dict(rows=1 << 31), dict(k=0), dict(k=12),
+               dict(n=4), dict(n=4100), dict(tile=32), dict(tile=96), dict(x=None), dict(w=None),
+               dict(off=None), dict(out=None), dict(x=p + 8), dict(w=p + 4), dict(out=p + 2),
+               dict(off=p + 2),
+               # more workgroups than one launch may have
+               dict(rows=(1 << 31) - 1, n=1 << 14, tile=64)):
+        assert call(**kw) == bad, kw
+    # nothing to do: accepted without touching the (null) buffers
+    assert call(rows=0, x=None, w=None, off=None, out=None) == L.MOE_OK
+
+
 def test_tuning_roundtrip_and_limits(lib):
     ctx, _, _ = _ctx(lib, _cfg())
     t = L.MoeTuning()

@@ -21,13 +21,14 @@ K distinct ids sampled without replacement; the slots keep the sampling order
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "make_batch", "replay_T", "replay_batch",
-    "x_to_torch_dtype_name",
+    "x_to_torch_dtype_name", "EXPERT_SHAPES", "expert_weights", "expert_rows",
 ]
 
 
@@ -168,3 +169,45 @@ def replay_batch(i: int, w: Workload = WORKLOADS["graph"]) -> dict:
     b = make_batch(w, T=T, seed=w.seed + i)
     b["T"] = T
     return b
+
+
+# Expert step (one linear map per expert between dispatch and combine). The
+# pages fix no expert width; "dsv3" uses DeepSeek-V3's routed-expert width
+# 2048, with gate and up projections fused: k_in = hidden 7168 -> n_out 4096.
+EXPERT_SHAPES = {
+    "dsv3": dict(workload="dsv3", k_in=7168, n_out=4096, seed=2024),
+}
+
+
+def expert_weights(E: int, n_out: int, k_in: int, seed: int) -> np.ndarray:
+    """uint16 [E, n_out, k_in] bf16 bit patterns: uniform random sign and
+    7-bit mantissa, exponent uniform over 2^-11 .. 2^-4 (magnitudes of a
+    k_in-wide linear layer's weights). Expert e draws raw 64-bit words from
+    its own stream (SeedSequence(seed).spawn(E)[e]), four 16-bit fields per
+    word, on a thread pool, so the 15 GB of the dsv3 shape take seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    out = np.empty((E, n_out, k_in), np.uint16)
+    n = n_out * k_in
+    words = (n + 3) // 4
+    keep = np.uint64(0x807F807F807F807F)      # sign and mantissa of 4 fields
+    low3 = np.uint64(0x0007000700070007)
+    bias = np.uint64(0x0074007400740074)      # 116 in every field
+    streams = np.random.SeedSequence(seed).spawn(E)
+
+    def fill(e):
+        rng = np.random.default_rng(streams[e])
+        w = rng.integers(0, 2 ** 64 - 1, size=words, dtype=np.uint64, endpoint=True)
+        w = (w & keep) | ((((w >> np.uint64(7)) & low3) + bias) << np.uint64(7))
+        out[e] = w.view(np.uint16)[:n].reshape(n_out, k_in)
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill, range(E)))
+    return out
+
+
+def expert_rows(rows: int, k_in: int, seed: int) -> np.ndarray:
+    """uint16 [rows, k_in] bf16 bits of N(0,1) draws (expert input rows)."""
+    rng = np.random.default_rng(seed)
+    return _draw_x(rng, rows, k_in, "bf16")
