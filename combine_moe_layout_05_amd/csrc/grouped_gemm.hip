@@ -10,12 +10,15 @@
 // the sum to bf16 (nearest even). Rows outside every segment are not written.
 //
 // Work split. A tile is (expert, 128 output features, up to BT rows of the
-// expert's segment); tiles are numbered expert by expert, row tiles fastest,
-// so row tiles that share a weight tile run side by side and share it in
-// cache. The grid covers the most tiles any routing can need,
-// ceil(max_rows / BT) + E row tiles per feature tile; wavefront 0 of each
+// expert's segment); tiles are numbered expert by expert, row tiles fastest.
+// Workgroups are dealt to the 8 XCDs round-robin, so each XCD is given a
+// contiguous run of tile numbers: row tiles that share a weight tile, and
+// feature tiles that share a row tile, then run side by side under one L2
+// and each operand is fetched from memory about once. The grid covers the
+// most tiles any routing can need, ceil(max_rows / BT) + E row tiles per
+// feature tile (rounded up to a multiple of 8); wavefront 0 of each
 // workgroup finds its tile from the offsets (a scan of the per-expert tile
-// counts over the 64 lanes) and workgroups past the last tile exit.
+// counts over the 64 lanes) and workgroups without a tile exit.
 //
 // Inside a tile, wavefront w owns features [32w, 32w + 32) and all BT rows:
 // v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand and the
@@ -38,10 +41,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256;
-constexpr int kStages = 4;          // even: the LDS buffer is the step's parity
+constexpr int kStages = 3;          // steps of loads in flight
 constexpr int kStepChunks = 8;   // 64 bf16 of k per step = 8 chunks of 16 bytes
+constexpr int kXcds = 8;         // MI355X: 8 XCDs, each with its own L2
 
 __device__ __forceinline__ bf16x8 as_bf16x8(v4i v) { return __builtin_bit_cast(bf16x8, v); }
+
+// LDS position of 16-byte chunk c of row r within the row's 128 bytes is
+// c ^ swz(r): any 16 consecutive rows at one chunk index land in 16 distinct
+// 16-byte bank groups (and any 8 in 8), so the B-fragment reads, one chunk
+// index per 32 rows, are free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // Rows [s0, s1) of expert e, clamped into [0, max_rows).
 __device__ __forceinline__ void segment(const int32_t* offsets, int32_t e, int32_t max_rows,
@@ -60,6 +70,7 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
                          int32_t chunks, int32_t N, int32_t ftiles, uint8_t* __restrict__ out) {
     constexpr int U = BT / 32;                       // 32-row sub-tiles
     __shared__ v4i xs[2][BT * kStepChunks];
+    __shared__ v4i ws[4][32 * kStepChunks];      // one weight slot per wavefront
     __shared__ int32_t info[4];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -81,11 +92,16 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
             const int64_t v = __shfl_up(incl, d, 64);
             if (lane >= d) incl += v;
         }
-        const int64_t u = blockIdx.x;
+        // Workgroup b runs on XCD b % kXcds (round-robin dispatch); XCD x
+        // takes the tile run [x * run, (x + 1) * run), so tiles that share a
+        // weight tile or a row tile meet in one L2.
         const int64_t total = __shfl(incl, 63, 64);
-        if (lane == 0 && u >= total) info[0] = -1;
+        const int64_t run = (total + kXcds - 1) / kXcds;
+        const int64_t idx = blockIdx.x / kXcds;
+        const int64_t u = (blockIdx.x % kXcds) * run + idx;
+        if (lane == 0 && (idx >= run || u >= total)) info[0] = -1;
         int64_t base = incl - local;
-        if (u >= base && u < incl) {
+        if (idx < run && u >= base && u < incl) {
             for (int e = e_lo; e < e_hi; ++e) {
                 int32_t s0, s1;
                 segment(offsets, e, max_rows, s0, s1);
@@ -111,58 +127,35 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
     const int32_t row0 = info[2];
     const int32_t nrows = info[3];
 
-    const int32_t steps = (chunks + kStepChunks - 1) / kStepChunks;
     const int h = lane >> 5;
     const int i = lane & 31;
-    // This lane's weight row (features past N read row N-1; never stored).
-    const int32_t f = min(f0 + wave * 32 + i, N - 1);
-    const v4i* wrow = w + (int64_t(e) * N + f) * chunks;
+    // Weight rows are loaded coalesced (8 lanes cover one row's 128-byte
+    // step, an instruction 8 rows) and staged through the wavefront's own
+    // LDS slot into the A-fragment layout: the fragment layout itself (32
+    // rows per instruction) costs the vector memory path about 3x more per
+    // byte. Lane l loads rows (l >> 3) + 8j, chunk l & 7; features past N
+    // read row N-1 (never stored).
+    const v4i* wrow[4];
+    int32_t wslot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (lane >> 3) + 8 * j;
+        const int c = lane & 7;
+        wrow[j] = w + (int64_t(e) * N + min(f0 + wave * 32 + r, N - 1)) * chunks + c;
+        wslot[j] = r * kStepChunks + (c ^ swz(r));
+    }
+    v4i* wbuf = ws[wave];
     // This thread's token-row chunks: q = tid + 256j of the BT x 8 step tile
     // (rows past the segment read its last row; never stored).
     const v4i* xrow[U];
-    int32_t xc[U];
     int32_t xslot[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
         const int q = tid + kGemmThreads * j;
         const int r = q >> 3;
         const int c = q & 7;
-        xrow[j] = x_e + int64_t(row0 + min(r, nrows - 1)) * chunks;
-        xc[j] = c;
-        xslot[j] = r * kStepChunks + (c ^ (r & 7));
-    }
-    // Every load is issued unconditionally (no divergent branches between
-    // the loads and their use): a chunk index past the row reads the row's
-    // last chunk and the value is replaced by zero, so steps past the end
-    // (the rounding of the loop to whole groups of kStages) add nothing.
-    const int32_t last = chunks - 1;
-    auto pick = [](bool ok, v4i v) {
-        v4i o;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) o[t] = ok ? v[t] : 0;
-        return o;
-    };
-    auto load_w = [&](int32_t step, v4i (&dst)[4]) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int32_t c = step * kStepChunks + 4 * h + s;
-            dst[s] = pick(c <= last, wrow[min(c, last)]);
-        }
-    };
-    auto load_x = [&](int32_t step, v4i (&dst)[U]) {
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int32_t c = step * kStepChunks + xc[j];
-            dst[j] = pick(c <= last, xrow[j][min(c, last)]);
-        }
-    };
-
-    v4i wr[kStages][4];
-    v4i xr[kStages][U];
-#pragma unroll
-    for (int p = 0; p < kStages; ++p) {
-        load_x(p, xr[p]);
-        load_w(p, wr[p]);
+        xrow[j] = x_e + int64_t(row0 + min(r, nrows - 1)) * chunks + c;
+        xslot[j] = r * kStepChunks + (c ^ swz(r));
     }
     f32x16 acc[U];
 #pragma unroll
@@ -170,27 +163,87 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-    for (int32_t s0 = 0; s0 < steps; s0 += kStages) {
+    // One step: rows of the step (already in registers) to LDS, then the
+    // 4 x U matrix-core products against the step's weight fragments.
+    auto mma_step = [&](int buf_id, const v4i (&wv)[4], const v4i (&xv)[U], auto&& after_barrier) {
+        v4i* buf = xs[buf_id];
+#pragma unroll
+        for (int j = 0; j < U; ++j) buf[xslot[j]] = xv[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wbuf[wslot[j]] = wv[j];
+        __syncthreads();
+        after_barrier();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bf16x8 a = as_bf16x8(wbuf[i * kStepChunks + ((4 * h + s) ^ swz(i))]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = u * 32 + i;
+                const bf16x8 b = as_bf16x8(buf[r * kStepChunks + ((4 * h + s) ^ swz(r))]);
+                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u], 0, 0, 0);
+            }
+        }
+    };
+
+    // Whole steps: every load is issued unconditionally, kStages steps ahead
+    // (the step index is clamped to the last whole step, a scalar, so the
+    // loop body has no divergent branches between the loads and their use).
+    const int32_t full = chunks / kStepChunks;
+    v4i wr[kStages][4];
+    v4i xr[kStages][U];
+    auto load_w = [&](int32_t step, v4i (&dst)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = wrow[j][step * kStepChunks];
+    };
+    auto load_x = [&](int32_t step, v4i (&dst)[U]) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) dst[j] = xrow[j][step * kStepChunks];
+    };
+    // The loop body runs whole groups of kStages steps with no branch in it
+    // (a branch there makes the wait counts conservative, which drains the
+    // pipeline every group); the 0..kStages-1 steps left over run after it
+    // from the already loaded ring.
+    int32_t done = 0;
+    if (full > 0) {
 #pragma unroll
         for (int p = 0; p < kStages; ++p) {
-            const int32_t step = s0 + p;
-            v4i* buf = xs[p & 1];            // kStages is even: p & 1 == step & 1
-#pragma unroll
-            for (int j = 0; j < U; ++j) buf[xslot[j]] = xr[p][j];
-            __syncthreads();
-            load_x(step + kStages, xr[p]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 a = as_bf16x8(wr[p][s]);
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int r = u * 32 + i;
-                    const bf16x8 b = as_bf16x8(buf[r * kStepChunks + ((4 * h + s) ^ (r & 7))]);
-                    acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u], 0, 0, 0);
-                }
-            }
-            load_w(step + kStages, wr[p]);
+            load_x(min(p, full - 1), xr[p]);
+            load_w(min(p, full - 1), wr[p]);
         }
+        int32_t s0 = 0;
+        for (; s0 + kStages <= full; s0 += kStages) {
+#pragma unroll
+            for (int p = 0; p < kStages; ++p) {
+                const int32_t ahead = min(s0 + p + kStages, full - 1);
+                mma_step((s0 + p) & 1, wr[p], xr[p], [&] { load_x(ahead, xr[p]); });
+                load_w(ahead, wr[p]);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kStages - 1; ++p)
+            if (s0 + p < full) mma_step((s0 + p) & 1, wr[p], xr[p], [] {});
+        done = full;
+    }
+    // The last, partial step (k_in not a multiple of 64): chunks past the
+    // row read as zero in both operands.
+    if (done * kStepChunks < chunks) {
+        const int32_t c0 = done * kStepChunks;
+        const int32_t last = chunks - 1;
+        v4i wv[4], xv[U];
+        const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int32_t c = c0 + (lane & 7);
+            const v4i v = wrow[j][min(c, last) - (lane & 7)];
+            wv[j] = c <= last ? v : zero;
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int32_t c = c0 + ((tid + kGemmThreads * j) & 7);
+            const v4i v = xrow[j][min(c, last) - ((tid + kGemmThreads * j) & 7)];
+            xv[j] = c <= last ? v : zero;
+        }
+        mma_step(done & 1, wv, xv, [] {});
     }
 
     // acc[u][4q + t] is out[row u*32 + i][feature 32w + 8q + 4h + t].

@@ -144,10 +144,12 @@ hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 
 // Expert step (grouped GEMM): workgroups of the launch for max_rows rows,
 // E experts, N output features and row tiles of row_tile rows: every
-// (feature tile of 128, row tile) pair the worst routing can need.
+// (feature tile of 128, row tile) pair the worst routing can need, rounded
+// up to a multiple of 8 (one run of tiles per XCD).
 inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile) {
     const int64_t ftiles = (int64_t(N) + 127) / 128;
-    return ftiles * ((max_rows + row_tile - 1) / row_tile + E);
+    const int64_t tiles = ftiles * ((max_rows + row_tile - 1) / row_tile + E);
+    return (tiles + 7) / 8 * 8;
 }
 constexpr int kGemmRowTileSmall = 64;
 constexpr int kGemmRowTileLarge = 128;
