@@ -7,7 +7,12 @@ reads the dispatched buffer), moe_combine. The default workload is the
 DeepSeek-V3-shaped layer (T=4096, D=7168, E=256, top-8, bf16, Zipf(1.1)
 routing). Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload dsv3]
+The line also carries, under "expert_step", the expert step between dispatch
+and combine (moe_grouped_gemm: one linear map per expert driven by the
+device-side offsets) at the workload's expert shape, timed over its own
+launches; it is not part of the step above.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsv3] [--expert-iters N]
 """
 from __future__ import annotations
 
@@ -25,10 +30,12 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "combine_moe_layout_05_amd", "csrc")
 KERNEL_SOURCES = {
-    "dispatch": ["dispatch.hip", "moe_kernels.h"],
+    "dispatch": ["dispatch.hip", "moe_lanes.h", "moe_kernels.h"],
     "combine": ["combine.hip", "moe_lanes.h", "moe_kernels.h"],
     "layout": ["layout.hip", "moe_kernels.h"],
+    "grouped_gemm": ["grouped_gemm.hip", "moe_lanes.h", "moe_kernels.h"],
 }
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak
 METRIC = ("dispatch+combine tokens/s and achieved HBM GB/s (% of peak), "
           "T=4096 D=7168 E=256 k=8")
 
@@ -59,6 +66,8 @@ def parse_args():
     p.add_argument("--combine-block-waves", type=int, default=0)
     p.add_argument("--backward", type=int, default=0,
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
+    p.add_argument("--expert-iters", type=int, default=10,
+                   help="time the expert step (grouped GEMM) over this many launches; 0 skips")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run plain device write/read/copy of this size (HBM ceiling, "
                         "counter scaling)")
@@ -133,6 +142,65 @@ def calibrate_copy(mib: int) -> None:
         us = e0.elapsed_time(e1) * 1e3 / reps
         res[name] = {"us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
     print(json.dumps(res), flush=True)
+
+
+def expert_algorithmic_bytes(counts, k_in: int, n_out: int) -> int:
+    """Algorithmic HBM bytes of one expert-step launch: the weights of every
+    expert with rows (each read once), the rows in (k_in bf16) and out (n_out
+    bf16), and the offsets."""
+    used = int((counts > 0).sum())
+    total = int(counts.sum())
+    return used * n_out * k_in * 2 + total * (k_in + n_out) * 2 + (counts.size + 1) * 4
+
+
+def time_expert_step(args, w, disp, ids, x, s, ntpr, dev) -> dict:
+    import numpy as np
+    import torch
+
+    import workloads
+    from combine_moe_layout_05_amd import grouped_gemm, round_up4
+
+    sh = workloads.EXPERT_SHAPES[w.name]
+    k_in, n_out = sh["k_in"], sh["n_out"]
+    log(f"expert step: {w.E} experts {k_in} -> {n_out}, weights {w.E * n_out * k_in * 2 / 1e9:.1f} GB")
+    wts = workloads.expert_weights(w.E, n_out, k_in, sh["seed"])
+    wd = torch.from_numpy(wts.view(np.int16)).to(dev).view(torch.bfloat16)
+    del wts
+    lay = disp.layout(ids, ntpr)
+    disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
+    rows = round_up4(ntpr) * w.K
+    x_e = disp.x_e[:rows]
+    out = torch.empty((rows, n_out), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        grouped_gemm(x_e, wd, lay.offsets, out)
+    stream = torch.cuda.current_stream(dev)        # the stream the launches go to
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.expert_iters + 1)]
+    ev[0].record(stream)
+    for i in range(args.expert_iters):
+        grouped_gemm(x_e, wd, lay.offsets, out)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(args.expert_iters)])) * 1e3
+    counts = lay.counts.cpu().numpy()
+    per_launch = expert_algorithmic_bytes(counts, k_in, n_out)
+    flops = 2.0 * int(counts.sum()) * k_in * n_out
+    achieved = per_launch / (us * 1e-6) / 1e9
+    del wd, out
+    torch.cuda.empty_cache()
+    log(f"expert step {us:.1f} us: {achieved:.0f} GB/s, {flops / (us * 1e-6) / 1e12:.0f} TFLOP/s")
+    return {
+        "workload": f"{w.name} experts: {w.E} x ({k_in} -> {n_out}) bf16, "
+                    f"{int(counts.sum())} routed rows in {int((counts > 0).sum())} experts",
+        "launches": args.expert_iters,
+        "avg_launch_us": round(us, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": counter_traffic("grouped_gemm", w.name),
+                     "kernel": "grouped_gemm",
+                     "algorithmic_bytes_per_launch": per_launch},
+        "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+        "frac_of_bf16_dense_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
 
 
 def main() -> int:
@@ -297,6 +365,10 @@ def main() -> int:
                                                     / (db * 1e-6) / 1e9, 1)}
         log(f"backward: combine_backward {cb:.1f} us, dispatch_backward {db:.1f} us")
 
+    expert = None
+    if args.expert_iters > 0 and w.name in workloads.EXPERT_SHAPES:
+        expert = time_expert_step(args, w, disp, ids, x, s, ntpr, dev)
+
     dominant = "dispatch" if avg["dispatch"] >= avg["combine"] else "combine"
     per_launch = bytes_per_token(w, dominant) * w.T
     achieved = per_launch / (avg[dominant] * 1e-3) / 1e9
@@ -355,6 +427,7 @@ def main() -> int:
         "cold_cache": cold,
         "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
         "backward": backward,
+        "expert_step": expert,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -10,27 +10,34 @@
 // the sum to bf16 (nearest even). Rows outside every segment are not written.
 //
 // Work split. A tile is (expert, 128 output features, up to BT rows of the
-// expert's segment); tiles are numbered expert by expert, row tiles fastest.
-// Workgroups are dealt to the 8 XCDs round-robin, so each XCD is given a
-// contiguous run of tile numbers: row tiles that share a weight tile, and
-// feature tiles that share a row tile, then run side by side under one L2
-// and each operand is fetched from memory about once. The grid covers the
-// most tiles any routing can need, ceil(max_rows / BT) + E row tiles per
-// feature tile (rounded up to a multiple of 8); wavefront 0 of each
-// workgroup finds its tile from the offsets (a scan of the per-expert tile
-// counts over the 64 lanes) and workgroups without a tile exit.
+// expert's segment). Within an expert, tiles go in blocks of up to 8 row
+// tiles: all feature tiles of a block, each with the block's row tiles
+// fastest. Workgroups are dealt to the 8 XCDs round-robin, so each XCD is
+// given a contiguous run of tile numbers; the ~64 workgroups an XCD runs at
+// once then cover about 8 row tiles x 8 feature tiles of one expert, which
+// share each weight tile and each row tile through that XCD's L2 (with a
+// plain feature-major order a large expert re-fetches its rows once per
+// feature tile). The grid covers the most tiles any routing can need,
+// ceil(max_rows / BT) + E row tiles per feature tile (rounded up to a
+// multiple of 8); wavefront 0 of each workgroup finds its tile from the
+// offsets (a scan of the per-expert tile counts over the 64 lanes) and
+// workgroups without a tile exit.
 //
 // Inside a tile, wavefront w owns features [32w, 32w + 32) and all BT rows:
 // v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand and the
-// token rows as B. The weight rows are read once per tile, straight into the
-// A fragments (they are not shared, so they skip LDS); the token rows, which
-// all four wavefronts need, go through LDS in 16-byte chunks whose position
-// within a 128-byte row is XOR-swizzled by the row index. Both are loaded
-// kStages steps of 64 k ahead into a register ring, weights and rows of a
-// step issued together, so waiting for a step's rows never waits for later
-// weights. Within a step, lane half h supplies k = 32h + 8s + j (s the
-// instruction, j the element) for both operands: any pairing of k slots
-// gives the same sum, and this one makes a lane's weight loads contiguous.
+// token rows as B. An MFMA fragment puts consecutive lanes on different rows,
+// and loads in that layout run at about a third of the rate of loads where
+// every 4 consecutive lanes read one contiguous 64-byte piece (measured on
+// MI355X from L2-resident data). So both operands are loaded coalesced (8
+// lanes per 128-byte step of a row) and re-laid out through LDS: the token
+// rows, which all four wavefronts read, into a shared buffer (double
+// buffered, one barrier per step); each wavefront's weight rows into its own
+// slot. 16-byte chunks sit in LDS at a position XOR-swizzled by the row
+// index, so fragment reads are free of bank conflicts. Loads run kStages
+// steps of 64 k ahead in a register ring, weights and rows of a step issued
+// together, so waiting for a step's rows never waits for later weights.
+// Within a step, lane half h supplies k = 32h + 8s + j (s the instruction, j
+// the element) for both operands: any pairing of k slots gives the same sum.
 #include "moe_kernels.h"
 #include "moe_lanes.h"
 
@@ -41,7 +48,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256;
-constexpr int kStages = 3;          // steps of loads in flight
+constexpr int kStages = 2;          // steps of loads in flight (more costs occupancy)
 constexpr int kStepChunks = 8;   // 64 bf16 of k per step = 8 chunks of 16 bytes
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, each with its own L2
 
@@ -108,10 +115,15 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
                 const int32_t mt = (s1 - s0 + BT - 1) / BT;
                 const int64_t n = int64_t(mt) * ftiles;
                 if (u < base + n) {
+                    // Within the expert: blocks of up to 8 row tiles; in a
+                    // block, feature tiles, then its row tiles.
                     const int32_t rem = static_cast<int32_t>(u - base);
-                    const int32_t r0 = s0 + (rem % mt) * BT;
+                    const int32_t mb = rem / (ftiles * 8);
+                    const int32_t in = rem - mb * ftiles * 8;
+                    const int32_t mbe = min(8, mt - mb * 8);
+                    const int32_t r0 = s0 + (mb * 8 + in % mbe) * BT;
                     info[0] = e;
-                    info[1] = (rem / mt) * 128;
+                    info[1] = (in / mbe) * 128;
                     info[2] = r0;
                     info[3] = min(BT, s1 - r0);
                     break;
