@@ -25,6 +25,8 @@ MOE_FLAG_BACKWARD = 1
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_WEIGHTS_ROW_MAJOR = 0
+MOE_WEIGHTS_TILED = 1
 
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
@@ -67,7 +69,9 @@ SIGNATURES = {
     "moe_combine_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp),
                                     C.POINTER(_vp)]),
     "moe_dispatch_backward": (_int, [_vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
-    "moe_grouped_gemm": (_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _i32, _vp]),
+    "moe_grouped_gemm": (_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _i32, _i32, _vp]),
+    "moe_tiled_weights_bytes": (_i64, [_i32, _i32, _i32]),
+    "moe_tile_expert_weights": (_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "moe_set_tuning": (_int, [_vp, C.POINTER(MoeTuning)]),
     "moe_get_tuning": (_int, [_vp, C.POINTER(MoeTuning)]),
     "moe_ceil_div": (_i64, [_i64, _i64]),

@@ -9,14 +9,14 @@
 // with bf16 inputs, fp32 accumulation on the matrix cores and one rounding of
 // the sum to bf16 (nearest even). Rows outside every segment are not written.
 //
-// Work split. A tile is (expert, 128 output features, up to BT rows of the
-// expert's segment). Within an expert, tiles go in blocks of up to 8 row
-// tiles: all feature tiles of a block, each with the block's row tiles
-// fastest. Workgroups are dealt to the 8 XCDs round-robin, so each XCD is
-// given a contiguous run of tile numbers; the ~64 workgroups an XCD runs at
-// once then cover about 8 row tiles x 8 feature tiles of one expert, which
-// share each weight tile and each row tile through that XCD's L2 (with a
-// plain feature-major order a large expert re-fetches its rows once per
+// Work split. A tile is (expert, F output features, up to BT rows of the
+// expert's segment), F = 32 per wavefront. Within an expert, tiles go in
+// blocks of up to 8 row tiles: all feature tiles of a block, each with the
+// block's row tiles fastest. Workgroups are dealt to the 8 XCDs round-robin,
+// so each XCD is given a contiguous run of tile numbers; the workgroups an
+// XCD runs at once then cover a few row tiles x feature tiles of one expert,
+// which share each weight tile and each row tile through that XCD's L2 (with
+// a plain feature-major order a large expert re-fetches its rows once per
 // feature tile). The grid covers the most tiles any routing can need,
 // ceil(max_rows / BT) + E row tiles per feature tile (rounded up to a
 // multiple of 8); wavefront 0 of each workgroup finds its tile from the
@@ -25,19 +25,26 @@
 //
 // Inside a tile, wavefront w owns features [32w, 32w + 32) and all BT rows:
 // v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand and the
-// token rows as B. An MFMA fragment puts consecutive lanes on different rows,
-// and loads in that layout run at about a third of the rate of loads where
-// every 4 consecutive lanes read one contiguous 64-byte piece (measured on
-// MI355X from L2-resident data). So both operands are loaded coalesced (8
-// lanes per 128-byte step of a row) and re-laid out through LDS: the token
-// rows, which all four wavefronts read, into a shared buffer (double
-// buffered, one barrier per step); each wavefront's weight rows into its own
-// slot. 16-byte chunks sit in LDS at a position XOR-swizzled by the row
-// index, so fragment reads are free of bank conflicts. Loads run kStages
-// steps of 64 k ahead in a register ring, weights and rows of a step issued
-// together, so waiting for a step's rows never waits for later weights.
-// Within a step, lane half h supplies k = 32h + 8s + j (s the instruction, j
-// the element) for both operands: any pairing of k slots gives the same sum.
+// token rows as B. Within a step of 64 k, lane half h supplies k = 32h + 8s +
+// j (s the instruction, j the element) for both operands: any pairing of k
+// slots gives the same sum. An MFMA fragment puts consecutive lanes on
+// different rows, and loads in that layout run at about a third of the rate
+// of loads where every 4 consecutive lanes read one contiguous 64-byte piece
+// (measured on MI355X from L2-resident data), so:
+//   - token rows, which every wavefront reads, are loaded coalesced (8 lanes
+//     per 128-byte step of a row) into a shared LDS buffer (double
+//     buffered, one barrier per step) and read back as fragments;
+//   - weights in the row-major layout [E][N][k_in] are loaded the same way
+//     into a per-wavefront LDS slot (4 wavefronts, 128 features per tile);
+//   - weights in the tiled layout (moe_tile_expert_weights: each 64-lane A
+//     fragment stored as one contiguous KiB) are loaded straight into the
+//     fragment registers, so 16 wavefronts (512 features per tile) share
+//     each row tile and the rows are re-read 4x less often.
+// 16-byte chunks sit in LDS at a position XOR-swizzled by the row index, so
+// fragment reads are free of bank conflicts. Loads run kStages steps ahead
+// in a register ring, weights and rows of a step issued together; the loop
+// body has no branch (a branch there makes the compiler's wait counts
+// conservative, which drains the pipeline every group).
 #include "moe_kernels.h"
 #include "moe_lanes.h"
 
@@ -47,16 +54,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmThreads = 256;
 constexpr int kStages = 2;          // steps of loads in flight (more costs occupancy)
-constexpr int kStepChunks = 8;   // 64 bf16 of k per step = 8 chunks of 16 bytes
-constexpr int kXcds = 8;         // MI355X: 8 XCDs, each with its own L2
+constexpr int kStepChunks = 8;      // 64 bf16 of k per step = 8 chunks of 16 bytes
+constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
 
 __device__ __forceinline__ bf16x8 as_bf16x8(v4i v) { return __builtin_bit_cast(bf16x8, v); }
 
 // LDS position of 16-byte chunk c of row r within the row's 128 bytes is
 // c ^ swz(r): any 16 consecutive rows at one chunk index land in 16 distinct
-// 16-byte bank groups (and any 8 in 8), so the B-fragment reads, one chunk
+// 16-byte bank groups (and any 8 in 8), so the fragment reads, one chunk
 // index per 32 rows, are free of bank conflicts.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -70,14 +76,18 @@ __device__ __forceinline__ void segment(const int32_t* offsets, int32_t e, int32
     s1 = b;
 }
 
-template <int BT>
-__global__ __launch_bounds__(kGemmThreads)
+template <int BT, int WAVES, bool TILED>
+__global__ __launch_bounds__(WAVES * 64)
 void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
                          const int32_t* __restrict__ offsets, int32_t E, int32_t max_rows,
                          int32_t chunks, int32_t N, int32_t ftiles, uint8_t* __restrict__ out) {
-    constexpr int U = BT / 32;                       // 32-row sub-tiles
-    __shared__ v4i xs[2][BT * kStepChunks];
-    __shared__ v4i ws[4][32 * kStepChunks];      // one weight slot per wavefront
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kFeatures = WAVES * 32;
+    constexpr int U = BT / 32;                                        // 32-row sub-tiles
+    constexpr int UX = (BT * kStepChunks + kThreads - 1) / kThreads;  // row chunks per thread
+    // Row buffer plus one dummy chunk per lane for threads past the tile.
+    __shared__ v4i xs[2][BT * kStepChunks + 64];
+    __shared__ v4i ws[TILED ? 1 : WAVES][32 * kStepChunks];          // row-major weight slots
     __shared__ int32_t info[4];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -100,8 +110,7 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
             if (lane >= d) incl += v;
         }
         // Workgroup b runs on XCD b % kXcds (round-robin dispatch); XCD x
-        // takes the tile run [x * run, (x + 1) * run), so tiles that share a
-        // weight tile or a row tile meet in one L2.
+        // takes the tile run [x * run, (x + 1) * run).
         const int64_t total = __shfl(incl, 63, 64);
         const int64_t run = (total + kXcds - 1) / kXcds;
         const int64_t idx = blockIdx.x / kXcds;
@@ -123,7 +132,7 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
                     const int32_t mbe = min(8, mt - mb * 8);
                     const int32_t r0 = s0 + (mb * 8 + in % mbe) * BT;
                     info[0] = e;
-                    info[1] = (in / mbe) * 128;
+                    info[1] = (in / mbe) * kFeatures;
                     info[2] = r0;
                     info[3] = min(BT, s1 - r0);
                     break;
@@ -141,33 +150,44 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
 
     const int h = lane >> 5;
     const int i = lane & 31;
-    // Weight rows are loaded coalesced (8 lanes cover one row's 128-byte
-    // step, an instruction 8 rows) and staged through the wavefront's own
-    // LDS slot into the A-fragment layout: the fragment layout itself (32
-    // rows per instruction) costs the vector memory path about 3x more per
-    // byte. Lane l loads rows (l >> 3) + 8j, chunk l & 7; features past N
-    // read row N-1 (never stored).
+    const int32_t steps_all = (chunks + kStepChunks - 1) / kStepChunks;
+
+    // Weights. Tiled: [E][ceil(N/32)][steps][4][64 lanes] chunks, this
+    // wavefront's 32-feature block (clamped into range; the extra features
+    // are never stored). Row-major: lane l loads rows (l >> 3) + 8j, chunk
+    // l & 7 of the wavefront's 32 rows (features past N read row N-1).
+    const v4i* wt = nullptr;
     const v4i* wrow[4];
     int32_t wslot[4];
+    v4i* wbuf = ws[TILED ? 0 : wave];
+    if constexpr (TILED) {
+        const int32_t nb = (N + 31) / 32;
+        const int32_t fb = min(f0 / 32 + wave, nb - 1);
+        wt = w + ((int64_t(e) * nb + fb) * steps_all) * 4 * 64 + lane;
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (lane >> 3) + 8 * j;
-        const int c = lane & 7;
-        wrow[j] = w + (int64_t(e) * N + min(f0 + wave * 32 + r, N - 1)) * chunks + c;
-        wslot[j] = r * kStepChunks + (c ^ swz(r));
+        for (int j = 0; j < 4; ++j) {
+            const int r = (lane >> 3) + 8 * j;
+            const int c = lane & 7;
+            wrow[j] = w + (int64_t(e) * N + min(f0 + wave * 32 + r, N - 1)) * chunks + c;
+            wslot[j] = r * kStepChunks + (c ^ swz(r));
+        }
     }
-    v4i* wbuf = ws[wave];
-    // This thread's token-row chunks: q = tid + 256j of the BT x 8 step tile
-    // (rows past the segment read its last row; never stored).
-    const v4i* xrow[U];
-    int32_t xslot[U];
+    // Token rows: thread chunk q = tid + kThreads*j of the BT x 8 step tile
+    // (rows past the segment read its last row and are never stored; threads
+    // past the tile load a real row too and write the dummy slot).
+    const v4i* xrow[UX];
+    int32_t xc[UX];
+    int32_t xslot[UX];
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-        const int q = tid + kGemmThreads * j;
-        const int r = q >> 3;
+    for (int j = 0; j < UX; ++j) {
+        const int q = tid + kThreads * j;
+        const int r = min(q >> 3, BT - 1);
         const int c = q & 7;
         xrow[j] = x_e + int64_t(row0 + min(r, nrows - 1)) * chunks + c;
-        xslot[j] = r * kStepChunks + (c ^ swz(r));
+        xc[j] = c;
+        xslot[j] = q < BT * kStepChunks ? r * kStepChunks + (c ^ swz(r))
+                                        : BT * kStepChunks + lane;
     }
     f32x16 acc[U];
 #pragma unroll
@@ -175,19 +195,25 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-    // One step: rows of the step (already in registers) to LDS, then the
-    // 4 x U matrix-core products against the step's weight fragments.
-    auto mma_step = [&](int buf_id, const v4i (&wv)[4], const v4i (&xv)[U], auto&& after_barrier) {
+    // One step: rows (and row-major weights) of the step, already in
+    // registers, to LDS; then the 4 x U matrix-core products.
+    auto mma_step = [&](int buf_id, const v4i (&wv)[4], const v4i (&xv)[UX], auto&& after_barrier) {
         v4i* buf = xs[buf_id];
 #pragma unroll
-        for (int j = 0; j < U; ++j) buf[xslot[j]] = xv[j];
+        for (int j = 0; j < UX; ++j) buf[xslot[j]] = xv[j];
+        if constexpr (!TILED) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wbuf[wslot[j]] = wv[j];
+            for (int j = 0; j < 4; ++j) wbuf[wslot[j]] = wv[j];
+        }
         __syncthreads();
         after_barrier();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const bf16x8 a = as_bf16x8(wbuf[i * kStepChunks + ((4 * h + s) ^ swz(i))]);
+            bf16x8 a;
+            if constexpr (TILED)
+                a = as_bf16x8(wv[s]);
+            else
+                a = as_bf16x8(wbuf[i * kStepChunks + ((4 * h + s) ^ swz(i))]);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = u * 32 + i;
@@ -197,24 +223,24 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
         }
     };
 
-    // Whole steps: every load is issued unconditionally, kStages steps ahead
-    // (the step index is clamped to the last whole step, a scalar, so the
-    // loop body has no divergent branches between the loads and their use).
     const int32_t full = chunks / kStepChunks;
     v4i wr[kStages][4];
-    v4i xr[kStages][U];
+    v4i xr[kStages][UX];
     auto load_w = [&](int32_t step, v4i (&dst)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = wrow[j][step * kStepChunks];
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (TILED)
+                dst[j] = wt[(step * 4 + j) * 64];
+            else
+                dst[j] = wrow[j][step * kStepChunks];
+        }
     };
-    auto load_x = [&](int32_t step, v4i (&dst)[U]) {
+    auto load_x = [&](int32_t step, v4i (&dst)[UX]) {
 #pragma unroll
-        for (int j = 0; j < U; ++j) dst[j] = xrow[j][step * kStepChunks];
+        for (int j = 0; j < UX; ++j) dst[j] = xrow[j][step * kStepChunks];
     };
-    // The loop body runs whole groups of kStages steps with no branch in it
-    // (a branch there makes the wait counts conservative, which drains the
-    // pipeline every group); the 0..kStages-1 steps left over run after it
-    // from the already loaded ring.
+    // The loop body runs whole groups of kStages steps with no branch in it;
+    // the 0..kStages-1 steps left over run after it from the loaded ring.
     int32_t done = 0;
     if (full > 0) {
 #pragma unroll
@@ -236,23 +262,28 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
             if (s0 + p < full) mma_step((s0 + p) & 1, wr[p], xr[p], [] {});
         done = full;
     }
-    // The last, partial step (k_in not a multiple of 64): chunks past the
-    // row read as zero in both operands.
+    // The last, partial step (k_in not a multiple of 64): row chunks past
+    // the row read as zero; row-major weight chunks too, tiled weights are
+    // zero there already.
     if (done * kStepChunks < chunks) {
         const int32_t c0 = done * kStepChunks;
         const int32_t last = chunks - 1;
-        v4i wv[4], xv[U];
         const v4i zero = {0, 0, 0, 0};
+        v4i wv[4], xv[UX];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int32_t c = c0 + (lane & 7);
-            const v4i v = wrow[j][min(c, last) - (lane & 7)];
-            wv[j] = c <= last ? v : zero;
+            if constexpr (TILED) {
+                wv[j] = wt[(done * 4 + j) * 64];
+            } else {
+                const int32_t c = c0 + (lane & 7);
+                const v4i v = wrow[j][min(c, last) - (lane & 7)];
+                wv[j] = c <= last ? v : zero;
+            }
         }
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int32_t c = c0 + ((tid + kGemmThreads * j) & 7);
-            const v4i v = xrow[j][min(c, last) - ((tid + kGemmThreads * j) & 7)];
+        for (int j = 0; j < UX; ++j) {
+            const int32_t c = c0 + xc[j];
+            const v4i v = xrow[j][min(c, last) - xc[j]];
             xv[j] = c <= last ? v : zero;
         }
         mma_step(done & 1, wv, xv, [] {});
@@ -276,14 +307,38 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
     }
 }
 
-template <int BT>
+// Tiled weight layout: chunk ((((e * NB + b) * S + t) * 4 + s) * 64 + l) holds
+// w[e][32b + (l & 31)][64t + 32(l >> 5) + 8s .. + 8] -- the A fragment of
+// lane l for instruction s of step t of feature block b -- or zeros where
+// the feature or the k index is past the matrix (NB = ceil(N/32), S =
+// ceil(k_in/64)). One thread per 16-byte output chunk.
+__global__ __launch_bounds__(256)
+void tile_weights_kernel(const v4i* __restrict__ src, int32_t N, int32_t chunks, int32_t NB,
+                         int32_t S, int64_t total, v4i* __restrict__ dst) {
+    const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (q >= total) return;
+    const int l = static_cast<int>(q & 63);
+    const int s = static_cast<int>((q >> 6) & 3);
+    const int64_t rest = q >> 8;
+    const int32_t t = static_cast<int32_t>(rest % S);
+    const int64_t eb = rest / S;
+    const int32_t b = static_cast<int32_t>(eb % NB);
+    const int64_t e = eb / NB;
+    const int32_t row = 32 * b + (l & 31);
+    const int32_t c = 8 * t + 4 * (l >> 5) + s;
+    v4i v = {0, 0, 0, 0};
+    if (row < N && c < chunks) v = src[(e * N + row) * chunks + c];
+    dst[q] = v;
+}
+
+template <int BT, int WAVES, bool TILED>
 hipError_t launch_bt(const GroupedGemmArgs& a, hipStream_t stream) {
-    const int64_t grid = grouped_gemm_grid(a.max_rows, a.E, a.N, BT);
-    hipLaunchKernelGGL((grouped_gemm_kernel<BT>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(kGemmThreads), 0, stream, static_cast<const v4i*>(a.x_e),
+    const int64_t grid = grouped_gemm_grid(a.max_rows, a.E, a.N, BT, WAVES * 32);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BT, WAVES, TILED>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(WAVES * 64), 0, stream, static_cast<const v4i*>(a.x_e),
                        static_cast<const v4i*>(a.w), a.offsets, a.E,
-                       static_cast<int32_t>(a.max_rows), a.Kd / 8,
-                       a.N, static_cast<int32_t>((a.N + 127) / 128),
+                       static_cast<int32_t>(a.max_rows), a.Kd / 8, a.N,
+                       static_cast<int32_t>((a.N + WAVES * 32 - 1) / (WAVES * 32)),
                        static_cast<uint8_t*>(a.out));
     return hipGetLastError();
 }
@@ -292,11 +347,30 @@ hipError_t launch_bt(const GroupedGemmArgs& a, hipStream_t stream) {
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     if (a.max_rows <= 0) return hipSuccess;
+    if (a.tiled) {
+        switch (a.row_tile) {
+            case 64: return launch_bt<64, kGemmWavesTiled, true>(a, stream);
+            case 128: return launch_bt<128, kGemmWavesTiled, true>(a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.row_tile) {
-        case 64: return launch_bt<64>(a, stream);
-        case 128: return launch_bt<128>(a, stream);
+        case 64: return launch_bt<64, kGemmWavesRowMajor, false>(a, stream);
+        case 128: return launch_bt<128, kGemmWavesRowMajor, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_tile_weights(const TileWeightsArgs& a, hipStream_t stream) {
+    const int64_t NB = (int64_t(a.N) + 31) / 32;
+    const int64_t S = (int64_t(a.Kd) + 63) / 64;
+    const int64_t total = int64_t(a.E) * NB * S * 256;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(tile_weights_kernel, dim3(static_cast<uint32_t>((total + 255) / 256)),
+                       dim3(256), 0, stream, static_cast<const v4i*>(a.src), a.N, a.Kd / 8,
+                       static_cast<int32_t>(NB), static_cast<int32_t>(S), total,
+                       static_cast<v4i*>(a.dst));
+    return hipGetLastError();
 }
 
 }  // namespace moe

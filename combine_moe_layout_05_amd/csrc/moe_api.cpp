@@ -445,19 +445,26 @@ int moe_dispatch_backward(moe_ctx* ctx, const void* d_grad_x_expert, const int32
 }
 
 
+static bool gemm_sizes_ok(int32_t num_experts, int32_t n_out, int32_t k_in) {
+    return num_experts >= 1 && num_experts <= MOE_MAX_EXPERTS && k_in >= 8 && k_in % 8 == 0 &&
+           n_out >= 8 && n_out % 8 == 0;
+}
+
+static bool misaligned(const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+
 int moe_grouped_gemm(const void* d_x_expert, const void* d_weights, const int32_t* d_offsets,
                      int32_t num_experts, int64_t max_rows, int32_t k_in, int32_t n_out,
-                     void* d_out, int32_t row_tile, void* stream) {
-    if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+                     void* d_out, int32_t row_tile, int32_t weight_layout, void* stream) {
+    if (!gemm_sizes_ok(num_experts, n_out, k_in)) return MOE_ERR_INVALID_ARG;
     if (max_rows < 0 || max_rows > INT32_MAX) return MOE_ERR_INVALID_ARG;
-    if (k_in < 8 || k_in % 8 != 0 || n_out < 8 || n_out % 8 != 0) return MOE_ERR_INVALID_ARG;
     if (row_tile != 0 && row_tile != moe::kGemmRowTileSmall && row_tile != moe::kGemmRowTileLarge)
+        return MOE_ERR_INVALID_ARG;
+    if (weight_layout != MOE_WEIGHTS_ROW_MAJOR && weight_layout != MOE_WEIGHTS_TILED)
         return MOE_ERR_INVALID_ARG;
     if (max_rows == 0) return MOE_OK;
     if (!d_x_expert || !d_weights || !d_offsets || !d_out) return MOE_ERR_INVALID_ARG;
-    auto misaligned = [](const void* p, uintptr_t a) {
-        return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
-    };
     if (misaligned(d_x_expert, 16) || misaligned(d_weights, 16) || misaligned(d_out, 16) ||
         misaligned(d_offsets, 4))
         return MOE_ERR_INVALID_ARG;
@@ -468,7 +475,10 @@ int moe_grouped_gemm(const void* d_x_expert, const void* d_weights, const int32_
     if (row_tile == 0)
         row_tile = max_rows >= int64_t(64) * num_experts ? moe::kGemmRowTileLarge
                                                          : moe::kGemmRowTileSmall;
-    if (moe::grouped_gemm_grid(max_rows, num_experts, n_out, row_tile) > INT32_MAX)
+    const bool tiled = weight_layout == MOE_WEIGHTS_TILED;
+    const int32_t features =
+        32 * (tiled ? moe::kGemmWavesTiled : moe::kGemmWavesRowMajor);
+    if (moe::grouped_gemm_grid(max_rows, num_experts, n_out, row_tile, features) > INT32_MAX)
         return MOE_ERR_INVALID_ARG;
     moe::GroupedGemmArgs a;
     a.x_e = d_x_expert;
@@ -479,8 +489,33 @@ int moe_grouped_gemm(const void* d_x_expert, const void* d_weights, const int32_
     a.Kd = k_in;
     a.N = n_out;
     a.row_tile = row_tile;
+    a.tiled = tiled;
     a.out = d_out;
     if (moe::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int64_t moe_tiled_weights_bytes(int32_t num_experts, int32_t n_out, int32_t k_in) {
+    if (!gemm_sizes_ok(num_experts, n_out, k_in)) return -1;
+    return moe::tiled_weights_bytes(num_experts, n_out, k_in);
+}
+
+int moe_tile_expert_weights(const void* d_weights, int32_t num_experts, int32_t n_out,
+                            int32_t k_in, void* d_tiled, void* stream) {
+    if (!gemm_sizes_ok(num_experts, n_out, k_in)) return MOE_ERR_INVALID_ARG;
+    if (!d_weights || !d_tiled || misaligned(d_weights, 16) || misaligned(d_tiled, 16))
+        return MOE_ERR_INVALID_ARG;
+    // one thread per 16-byte chunk; the grid must fit one launch
+    if (moe::tiled_weights_bytes(num_experts, n_out, k_in) / 16 / 256 >= INT32_MAX)
+        return MOE_ERR_INVALID_ARG;
+    moe::TileWeightsArgs a;
+    a.src = d_weights;
+    a.E = num_experts;
+    a.N = n_out;
+    a.Kd = k_in;
+    a.dst = d_tiled;
+    if (moe::launch_tile_weights(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

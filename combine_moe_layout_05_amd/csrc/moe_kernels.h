@@ -143,28 +143,47 @@ struct TopkFromMapArgs {
 hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 
 // Expert step (grouped GEMM): workgroups of the launch for max_rows rows,
-// E experts, N output features and row tiles of row_tile rows: every
-// (feature tile of 128, row tile) pair the worst routing can need, rounded
-// up to a multiple of 8 (one run of tiles per XCD).
-inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile) {
-    const int64_t ftiles = (int64_t(N) + 127) / 128;
+// E experts, N output features, row tiles of row_tile rows and feature tiles
+// of `features`: every (feature tile, row tile) pair the worst routing can
+// need, rounded up to a multiple of 8 (one run of tiles per XCD).
+inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile,
+                                 int32_t features) {
+    const int64_t ftiles = (int64_t(N) + features - 1) / features;
     const int64_t tiles = ftiles * ((max_rows + row_tile - 1) / row_tile + E);
     return (tiles + 7) / 8 * 8;
 }
 constexpr int kGemmRowTileSmall = 64;
 constexpr int kGemmRowTileLarge = 128;
+// Wavefronts per workgroup (32 output features each): row-major weights are
+// staged through LDS per wavefront; tiled weights go straight to registers.
+constexpr int kGemmWavesRowMajor = 4;
+constexpr int kGemmWavesTiled = 16;
 
 struct GroupedGemmArgs {
     const void* x_e;        // [max_rows][Kd] bf16
-    const void* w;          // [E][N][Kd] bf16
+    const void* w;          // [E][N][Kd] bf16, or the tiled form of it
     const int32_t* offsets; // [E+1], device
     int32_t E;
     int64_t max_rows;       // <= INT32_MAX
     int32_t Kd;             // multiple of 8
     int32_t N;              // multiple of 8
     int32_t row_tile;       // kGemmRowTileSmall or kGemmRowTileLarge
+    bool tiled;             // w is in the tiled layout
     void* out;              // [max_rows][N] bf16
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream);
+
+// Tiled weight layout: [E][ceil(N/32)][ceil(Kd/64)][4][64] chunks of 16 bytes.
+inline int64_t tiled_weights_bytes(int32_t E, int32_t N, int32_t Kd) {
+    return int64_t(E) * ((int64_t(N) + 31) / 32) * ((int64_t(Kd) + 63) / 64) * 256 * 16;
+}
+struct TileWeightsArgs {
+    const void* src;        // [E][N][Kd] bf16
+    int32_t E;
+    int32_t N;              // multiple of 8
+    int32_t Kd;             // multiple of 8
+    void* dst;              // tiled_weights_bytes(E, N, Kd) bytes
+};
+hipError_t launch_tile_weights(const TileWeightsArgs& a, hipStream_t stream);
 
 }  // namespace moe

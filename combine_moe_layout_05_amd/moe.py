@@ -60,19 +60,57 @@ def validate_num_max(configured: int, derived: int) -> None:
     L.check(L.load().moe_validate_num_max(configured, derived), "validate_num_max")
 
 
-def grouped_gemm(x_expert: torch.Tensor, weights: torch.Tensor, offsets: torch.Tensor,
+class TiledExpertWeights(NamedTuple):
+    """Expert weights in the matrix-core tile order (moe_tile_expert_weights)."""
+    data: torch.Tensor       # uint8 [moe_tiled_weights_bytes], device
+    num_experts: int
+    n_out: int
+    k_in: int
+
+
+def tile_expert_weights(weights: torch.Tensor) -> TiledExpertWeights:
+    """One-time rewrite of bf16 [E, n_out, k_in] expert weights into the tile
+    order the expert step reads fastest (moe_tile_expert_weights)."""
+    if weights.dtype != torch.bfloat16 or weights.dim() != 3 or not weights.is_contiguous():
+        raise ValueError("weights must be a contiguous bf16 [E, n_out, k_in] tensor")
+    E, n_out, k_in = weights.shape
+    lib = L.load()
+    nbytes = int(lib.moe_tiled_weights_bytes(E, n_out, k_in))
+    if nbytes < 0:
+        raise ValueError(f"unsupported expert weight shape {tuple(weights.shape)}")
+    data = torch.empty(nbytes, dtype=torch.uint8, device=weights.device)
+    L.check(lib.moe_tile_expert_weights(weights.data_ptr(), E, n_out, k_in, data.data_ptr(),
+                                        _stream(weights.device)), "moe_tile_expert_weights")
+    return TiledExpertWeights(data, E, n_out, k_in)
+
+
+def grouped_gemm(x_expert: torch.Tensor, weights, offsets: torch.Tensor,
                  out: Optional[torch.Tensor] = None, *, row_tile: int = 0) -> torch.Tensor:
     """Expert step between dispatch and combine (moe_grouped_gemm): for each
     expert e, rows r in [offsets[e], offsets[e+1]) get
-    out[r] = x_expert[r] @ weights[e].T (fp32 accumulation, one rounding to
-    bf16). offsets stays on the device (e.g. Layout.offsets); rows outside
-    every segment keep what `out` held.
+    out[r] = x_expert[r] @ W[e].T (fp32 accumulation, one rounding to bf16).
+    offsets stays on the device (e.g. Layout.offsets); rows outside every
+    segment keep what `out` held.
 
-    x_expert bf16 [R, k_in]; weights bf16 [E, n_out, k_in]; offsets int32
-    [E+1]; out bf16 [R, n_out] (allocated with torch.empty if None)."""
+    x_expert bf16 [R, k_in]; weights bf16 [E, n_out, k_in] or the
+    TiledExpertWeights of them (same results, faster); offsets int32 [E+1];
+    out bf16 [R, n_out] (allocated with torch.empty if None)."""
     dev = x_expert.device
+    if isinstance(weights, TiledExpertWeights):
+        E, n_out, k_in = weights.num_experts, weights.n_out, weights.k_in
+        w_t, layout = weights.data, L.MOE_WEIGHTS_TILED
+        if w_t.device != dev:
+            raise ValueError(f"weights must be on {dev}, got {w_t.device}")
+    else:
+        if weights.device != dev:
+            raise ValueError(f"weights must be on {dev}, got {weights.device}")
+        if weights.dtype != torch.bfloat16:
+            raise TypeError(f"weights must be torch.bfloat16, got {weights.dtype}")
+        if weights.dim() != 3 or not weights.is_contiguous():
+            raise ValueError("weights must be a contiguous 3-d tensor")
+        E, n_out, k_in = weights.shape
+        w_t, layout = weights, L.MOE_WEIGHTS_ROW_MAJOR
     for name, t, dt, dim in (("x_expert", x_expert, torch.bfloat16, 2),
-                             ("weights", weights, torch.bfloat16, 3),
                              ("offsets", offsets, torch.int32, 1)):
         if t.device != dev:
             raise ValueError(f"{name} must be on {dev}, got {t.device}")
@@ -80,7 +118,6 @@ def grouped_gemm(x_expert: torch.Tensor, weights: torch.Tensor, offsets: torch.T
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
         if t.dim() != dim or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dim}-d tensor")
-    E, n_out, k_in = weights.shape
     R = x_expert.shape[0]
     if x_expert.shape[1] != k_in or offsets.shape[0] != E + 1:
         raise ValueError("shapes: x_expert [R, k_in], weights [E, n_out, k_in], offsets [E+1]")
@@ -89,8 +126,8 @@ def grouped_gemm(x_expert: torch.Tensor, weights: torch.Tensor, offsets: torch.T
     elif (out.device != dev or out.dtype != torch.bfloat16 or tuple(out.shape) != (R, n_out)
           or not out.is_contiguous()):
         raise ValueError(f"out must be a contiguous bf16 [{R}, {n_out}] tensor on {dev}")
-    L.check(L.load().moe_grouped_gemm(x_expert.data_ptr(), weights.data_ptr(), offsets.data_ptr(),
-                                      E, R, k_in, n_out, out.data_ptr(), int(row_tile),
+    L.check(L.load().moe_grouped_gemm(x_expert.data_ptr(), w_t.data_ptr(), offsets.data_ptr(),
+                                      E, R, k_in, n_out, out.data_ptr(), int(row_tile), layout,
                                       _stream(dev)), "moe_grouped_gemm")
     return out
 

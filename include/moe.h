@@ -261,6 +261,10 @@ int moe_dispatch_backward(moe_ctx *ctx, const void *d_grad_x_expert, const int32
                           int32_t T, int32_t num_tokens_per_rank, void *stream,
                           void **d_grad_x_out);
 
+/* Weight layouts the expert step reads. */
+#define MOE_WEIGHTS_ROW_MAJOR 0 /* [num_experts][n_out][k_in] bf16 */
+#define MOE_WEIGHTS_TILED     1 /* the output of moe_tile_expert_weights */
+
 /* Expert step between dispatch and combine ([UC] "Tests": layout, dispatch,
  * expert and combine captured in one graph; "Internode" item 2: the expert
  * step takes its per-expert row counts from device memory, with no host
@@ -269,11 +273,16 @@ int moe_dispatch_backward(moe_ctx *ctx, const void *d_grad_x_expert, const int32
  * offsets[e] <= r < offsets[e+1],
  *   out[r][n] = sum over d < k_in of x_expert[r][d] * weights[e][n][d]
  * bf16 inputs, fp32 accumulation (matrix cores; summation order not
- * specified), rounded once to bf16 (nearest even). Rows outside every
- * segment are not written. Needs no context and no workspace.
+ * specified, the same for both layouts), rounded once to bf16 (nearest
+ * even). Rows outside every segment are not written. Needs no context and
+ * no workspace.
  *   d_x_expert  bf16 [max_rows][k_in]  (x_e of moe_dispatch when k_in = hidden)
- *   d_weights   bf16 [num_experts][n_out][k_in]  (expert e's weight as n_out
- *               rows of k_in: a linear layer's [out][in] layout)
+ *   d_weights   weight_layout MOE_WEIGHTS_ROW_MAJOR: bf16
+ *               [num_experts][n_out][k_in] (expert e's weight as n_out rows
+ *               of k_in: a linear layer's [out][in] layout);
+ *               MOE_WEIGHTS_TILED: the same weights rewritten once by
+ *               moe_tile_expert_weights (faster: read straight into the
+ *               matrix-core operand registers)
  *   d_offsets   int32 [num_experts + 1] in device memory, read only by the
  *               kernel: a non-decreasing prefix sum from 0 with
  *               offsets[num_experts] <= max_rows (the context's offsets
@@ -293,7 +302,25 @@ int moe_dispatch_backward(moe_ctx *ctx, const void *d_grad_x_expert, const int32
  * MOE_ERR_INVALID_ARG. */
 int moe_grouped_gemm(const void *d_x_expert, const void *d_weights, const int32_t *d_offsets,
                      int32_t num_experts, int64_t max_rows, int32_t k_in, int32_t n_out,
-                     void *d_out, int32_t row_tile, void *stream);
+                     void *d_out, int32_t row_tile, int32_t weight_layout, void *stream);
+
+/* Bytes of the tiled form of [num_experts][n_out][k_in] bf16 weights:
+ * num_experts * ceil(n_out/32)*32 * ceil(k_in/64)*64 * 2 (zero padded), or
+ * -1 for sizes moe_grouped_gemm does not take. Pure host. */
+int64_t moe_tiled_weights_bytes(int32_t num_experts, int32_t n_out, int32_t k_in);
+
+/* Rewrites row-major expert weights into the tiled layout (a one-time
+ * permutation with zero padding; the weights are static): for feature
+ * block b (32 features), k step t (64 elements), instruction s (0..3) and
+ * lane l (0..63), 16-byte chunk ((((e*NB + b)*S + t)*4 + s)*64 + l) holds
+ * weights[e][32b + l%32][64t + 32(l/32) + 8s .. +8], zeros past n_out or
+ * k_in (NB = ceil(n_out/32), S = ceil(k_in/64)).
+ *   d_weights  bf16 [num_experts][n_out][k_in], device, 16-byte aligned
+ *   d_tiled    moe_tiled_weights_bytes(...) bytes, device, 16-byte aligned,
+ *              not overlapping d_weights
+ * Same size limits as moe_grouped_gemm; MOE_ERR_INVALID_ARG otherwise. */
+int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t n_out,
+                            int32_t k_in, void *d_tiled, void *stream);
 
 /* Launch shape tuning (optional). Each token row is split into `segments`
  * wavefront work items (1..16) and `block_waves` wavefronts (1..16) form a

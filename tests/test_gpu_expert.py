@@ -18,7 +18,8 @@ import torch
 
 import oracle
 import workloads
-from combine_moe_layout_05_amd import MoeDispatcher, MoeError, grouped_gemm, round_up4
+from combine_moe_layout_05_amd import (MoeDispatcher, MoeError, grouped_gemm, round_up4,
+                                       tile_expert_weights)
 
 from gpu_util import DEV, ORACLE_THREADS, f32_dev, i32_dev, note, sync_or_fail, x_to_dev, x_to_np
 
@@ -54,8 +55,10 @@ def _assert_within_bound(got_bits, exact, mag, k_in, what):
     return float(np.mean(got_bits == oracle.f64_to_bf16(exact)))
 
 
-def _run(x_e, w, off, max_rows, row_tile, out_fill=-1):
+def _run(x_e, w, off, max_rows, row_tile, out_fill=-1, tiled=False):
     xd, wd = x_to_dev(x_e), x_to_dev(w)
+    if tiled:
+        wd = tile_expert_weights(wd)
     out = torch.full((max_rows, w.shape[1]), out_fill, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     grouped_gemm(xd, wd, i32_dev(off), out, row_tile=row_tile)
     sync_or_fail()
@@ -71,9 +74,10 @@ SMALL = [  # E, counts (None = random), k_in, n_out
 ]
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("row_tile", [64, 128, 0])
 @pytest.mark.parametrize("case", range(len(SMALL)))
-def test_grouped_gemm_small_shapes(case, row_tile):
+def test_grouped_gemm_small_shapes(case, row_tile, tiled):
     E, counts, k_in, n_out = SMALL[case]
     rng = np.random.default_rng(100 + case)
     if counts is None:
@@ -84,8 +88,9 @@ def test_grouped_gemm_small_shapes(case, row_tile):
     max_rows = total + 37                    # rows past the total must stay untouched
     x = workloads.expert_rows(max_rows, k_in, 7 + case)
     w = workloads.expert_weights(E, n_out, k_in, 11 + case)
-    note(f"grouped_gemm E={E} k_in={k_in} n_out={n_out} total={total} row_tile={row_tile}")
-    got = _run(x, w, off, max_rows, row_tile)
+    note(f"grouped_gemm E={E} k_in={k_in} n_out={n_out} total={total} row_tile={row_tile} "
+         f"tiled={tiled}")
+    got = _run(x, w, off, max_rows, row_tile, tiled=tiled)
     exact = oracle.grouped_gemm(x, w, off, ORACLE_THREADS)
     mag = np.zeros_like(exact)
     ax, aw = np.abs(_f64(x)), np.abs(_f64(w))
@@ -103,12 +108,32 @@ def test_grouped_gemm_row_tiles_agree_bitwise_and_repeat():
     off = _offsets(rng.integers(0, 200, E))
     x = workloads.expert_rows(int(off[-1]), k_in, 1)
     w = workloads.expert_weights(E, n_out, k_in, 2)
-    note("grouped_gemm row tiles 64 vs 128")
+    note("grouped_gemm row tiles 64 vs 128, row-major vs tiled weights")
     a = _run(x, w, off, int(off[-1]), 64)
     b = _run(x, w, off, int(off[-1]), 128)
     c = _run(x, w, off, int(off[-1]), 64, out_fill=0)
-    assert np.array_equal(a, b)
-    assert np.array_equal(a, c)
+    d = _run(x, w, off, int(off[-1]), 128, tiled=True)
+    f = _run(x, w, off, int(off[-1]), 64, tiled=True)
+    for other in (b, c, d, f):
+        assert np.array_equal(a, other)
+
+
+@pytest.mark.parametrize("E,n_out,k_in", [(3, 200, 72), (2, 64, 128), (1, 8, 8)])
+def test_tiled_weight_layout(E, n_out, k_in):
+    """The tiled form against the layout's definition, built with numpy:
+    chunk (((e*NB + b)*S + t)*4 + s)*64 + l = w[e][32b + l%32][64t + 32(l//32)
+    + 8s : +8], zero past n_out / k_in."""
+    w = workloads.expert_weights(E, n_out, k_in, 9)
+    NB, S = -(-n_out // 32), -(-k_in // 64)
+    pad = np.zeros((E, NB * 32, S * 64), np.uint16)
+    pad[:, :n_out, :k_in] = w
+    ref = pad.reshape(E, NB, 32, S, 2, 4, 8).transpose(0, 1, 3, 5, 4, 2, 6).reshape(-1)
+    note(f"tile layout E={E} n_out={n_out} k_in={k_in}")
+    t = tile_expert_weights(x_to_dev(w))
+    sync_or_fail()
+    got = t.data.cpu().numpy().view(np.uint16)
+    assert got.size == ref.size
+    assert np.array_equal(got, ref)
 
 
 def test_grouped_gemm_edge_offsets():
@@ -157,6 +182,7 @@ def test_grouped_gemm_dsv3_full_size_sampled():
     note("dsv3 expert weights")
     w = workloads.expert_weights(wl.E, n_out, k_in, sh["seed"])
     wd = x_to_dev(w)
+    wt = tile_expert_weights(wd)
     disp = MoeDispatcher(wl.nmax, wl.D, wl.E, wl.K, dtype=torch.bfloat16, device=DEV)
     ids_d, s_d = i32_dev(b["ids"]), f32_dev(b["scores"])
     note("dsv3 layout + dispatch + grouped_gemm")
@@ -164,12 +190,17 @@ def test_grouped_gemm_dsv3_full_size_sampled():
     dsp = disp.dispatch(x_to_dev(b["x"]), s_d, ids_d, lay.counts, num_tokens_per_rank=wl.ntpr)
     max_rows = round_up4(wl.ntpr) * wl.K
     out = torch.full((max_rows, n_out), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
-    grouped_gemm(dsp.x_e, wd, lay.offsets, out)
+    grouped_gemm(dsp.x_e, wt, lay.offsets, out)
+    out_rm = torch.full_like(out, 0)
+    grouped_gemm(dsp.x_e, wd, lay.offsets, out_rm)
     sync_or_fail(120)
     total = int(lay.offsets[-1].item())
     ov = out.view(torch.int16)
     assert not bool((ov[:total] == -1).any()), "a row of the segments was not written"
     assert bool((ov[total:] == -1).all()), "a row past the total was written"
+    # the two weight layouts run the same products in the same order
+    assert bool(torch.equal(ov[:total], out_rm.view(torch.int16)[:total]))
+    del out_rm
     got_off = lay.offsets.cpu().numpy()
 
     lo = oracle.layout(b["ids"], wl.T, wl.ntpr, wl.E, wl.K)
@@ -190,7 +221,7 @@ def test_grouped_gemm_dsv3_full_size_sampled():
     mag = np.sum(ax * aw, axis=1)
     got = x_to_np(out[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
     _assert_within_bound(got, exact, mag, k_in, "dsv3 samples")
-    del disp, wd, out, dsp
+    del disp, wd, wt, out, dsp
     _free()
 
 
@@ -220,15 +251,18 @@ def _gpu_layer(disp, x, ids, scores, wd, T, ntpr, h):
     return disp.combine(h[:n], lay.row_map, s_d, num_tokens_per_rank=ntpr)
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("T,ntpr", [(614, 2048), (2047, 2048), (5, 8)])
-def test_layer_with_scaled_identity_experts_is_exact(T, ntpr):
+def test_layer_with_scaled_identity_experts_is_exact(T, ntpr, tiled):
     nmax, D, E, K = 2048, 512, 64, 8
     x, ids, scores = _dyadic_batch(nmax, D, E, K, 21)
     w = _identity_experts(E, D)
     wd = x_to_dev(w)
+    if tiled:
+        wd = tile_expert_weights(wd)
     disp = MoeDispatcher(nmax, D, E, K, dtype=torch.bfloat16, device=DEV)
     h = torch.empty((round_up4(nmax) * K, D), dtype=torch.bfloat16, device=DEV)
-    note(f"layer scaled identity T={T} ntpr={ntpr}")
+    note(f"layer scaled identity T={T} ntpr={ntpr} tiled={tiled}")
     y = x_to_np(_gpu_layer(disp, x, ids, scores, wd, T, ntpr, h))
     ref = oracle.run_layer(x, ids, scores, w, T, ntpr, E, K, ORACLE_THREADS)
     assert np.array_equal(y, ref["y"])
@@ -242,7 +276,7 @@ def test_layer_graph_replays_with_fresh_routing():
     oracle's layer, with eager calls on the same buffers in between."""
     nmax, D, E, K = 512, 256, 32, 4
     w = _identity_experts(E, D)
-    wd = x_to_dev(w)
+    wd = tile_expert_weights(x_to_dev(w))
     disp = MoeDispatcher(nmax, D, E, K, dtype=torch.bfloat16, device=DEV)
     n = round_up4(nmax) * K
     h = torch.empty((n, D), dtype=torch.bfloat16, device=DEV)

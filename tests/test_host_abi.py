@@ -211,23 +211,39 @@ def test_variant_calls_reject_bad_arguments(lib):
 
 def test_grouped_gemm_rejects_bad_arguments(lib):
     p = 1 << 41                                   # 16-byte aligned, never dereferenced
-    ok = dict(x=p, w=p, off=p, E=256, rows=32768, k=7168, n=4096, out=p, tile=0)
+    ok = dict(x=p, w=p, off=p, E=256, rows=32768, k=7168, n=4096, out=p, tile=0, lay=0)
 
     def call(**kw):
         a = dict(ok, **kw)
         return lib.moe_grouped_gemm(a["x"], a["w"], a["off"], a["E"], a["rows"], a["k"], a["n"],
-                                    a["out"], a["tile"], None)
+                                    a["out"], a["tile"], a["lay"], None)
 
     bad = L.MOE_ERR_INVALID_ARG
     for kw in (dict(E=0), dict(E=1025), dict(rows=-1), dict(rows=1 << 31), dict(k=0), dict(k=12),
-               dict(n=4), dict(n=4100), dict(tile=32), dict(tile=96), dict(x=None), dict(w=None),
-               dict(off=None), dict(out=None), dict(x=p + 8), dict(w=p + 4), dict(out=p + 2),
-               dict(off=p + 2),
+               dict(n=4), dict(n=4100), dict(tile=32), dict(tile=96), dict(lay=2), dict(lay=-1),
+               dict(x=None), dict(w=None), dict(off=None), dict(out=None), dict(x=p + 8),
+               dict(w=p + 4), dict(out=p + 2), dict(off=p + 2),
                # more workgroups than one launch may have
                dict(rows=(1 << 31) - 1, n=1 << 14, tile=64)):
         assert call(**kw) == bad, kw
     # nothing to do: accepted without touching the (null) buffers
     assert call(rows=0, x=None, w=None, off=None, out=None) == L.MOE_OK
+    assert call(rows=0, x=None, w=None, off=None, out=None, lay=1) == L.MOE_OK
+
+
+def test_tiled_weight_size_and_argument_checks(lib):
+    # E * ceil(n/32)*32 * ceil(k/64)*64 * 2 bytes (zero padded)
+    for E, n, k in ((256, 4096, 7168), (5, 200, 72), (1, 8, 8), (1024, 8, 64)):
+        assert lib.moe_tiled_weights_bytes(E, n, k) == E * (-(-n // 32) * 32) * (-(-k // 64) * 64) * 2
+    for E, n, k in ((0, 8, 8), (1025, 8, 8), (1, 4, 8), (1, 8, 12), (1, 8, 0)):
+        assert lib.moe_tiled_weights_bytes(E, n, k) == -1
+    p = 1 << 41
+    bad = L.MOE_ERR_INVALID_ARG
+    assert lib.moe_tile_expert_weights(None, 4, 64, 64, p, None) == bad
+    assert lib.moe_tile_expert_weights(p, 4, 64, 64, None, None) == bad
+    assert lib.moe_tile_expert_weights(p + 8, 4, 64, 64, p, None) == bad
+    assert lib.moe_tile_expert_weights(p, 4, 60, 64, p, None) == bad
+    assert lib.moe_tile_expert_weights(p, 0, 64, 64, p, None) == bad
 
 
 def test_tuning_roundtrip_and_limits(lib):
