@@ -188,22 +188,30 @@ def time_expert_step(args, w, disp, ids, x, s, ntpr, dev) -> dict:
     per_launch = expert_algorithmic_bytes(counts, k_in, n_out)
     flops = 2.0 * int(counts.sum()) * k_in * n_out
     achieved = per_launch / (us * 1e-6) / 1e9
+    tflops = flops / (us * 1e-6) / 1e12
     del wt, out
     torch.cuda.empty_cache()
-    log(f"expert step {us:.1f} us: {achieved:.0f} GB/s, {flops / (us * 1e-6) / 1e12:.0f} TFLOP/s")
+    log(f"expert step {us:.1f} us: {achieved:.0f} GB/s, {tflops:.0f} TFLOP/s")
+    # Bound by arithmetic intensity against the ridge peak_flops / peak_bytes.
+    if flops / per_launch > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_flops_per_launch": flops}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    roof.update({"traffic": counter_traffic("grouped_gemm", w.name), "kernel": "grouped_gemm",
+                 "algorithmic_bytes_per_launch": per_launch})
     return {
         "workload": f"{w.name} experts: {w.E} x ({k_in} -> {n_out}) bf16, "
                     f"{int(counts.sum())} routed rows in {int((counts > 0).sum())} experts",
         "weights": "tiled (moe_tile_expert_weights, once, untimed)",
         "launches": args.expert_iters,
         "avg_launch_us": round(us, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": counter_traffic("grouped_gemm", w.name),
-                     "kernel": "grouped_gemm",
-                     "algorithmic_bytes_per_launch": per_launch},
-        "tflops": round(flops / (us * 1e-6) / 1e12, 1),
-        "frac_of_bf16_dense_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "hbm_gbps": round(achieved, 1),
+        "tflops": round(tflops, 1),
+        "frac_of_bf16_dense_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
     }
 
 

@@ -176,6 +176,8 @@ def replay_batch(i: int, w: Workload = WORKLOADS["graph"]) -> dict:
 # 2048, with gate and up projections fused: k_in = hidden 7168 -> n_out 4096.
 EXPERT_SHAPES = {
     "dsv3": dict(workload="dsv3", k_in=7168, n_out=4096, seed=2024),
+    "prefill32k_zipf": dict(workload="prefill32k_zipf", k_in=7168, n_out=4096, seed=2024),
+    "prefill32k_uniform": dict(workload="prefill32k_uniform", k_in=7168, n_out=4096, seed=2024),
 }
 
 
