@@ -101,6 +101,12 @@ def grouped_gemm(x_expert: torch.Tensor, weights, offsets: torch.Tensor,
         w_t, layout = weights.data, L.MOE_WEIGHTS_TILED
         if w_t.device != dev:
             raise ValueError(f"weights must be on {dev}, got {w_t.device}")
+        # the kernel trusts the tiled buffer's size: check it here
+        need = int(L.load().moe_tiled_weights_bytes(E, n_out, k_in))
+        if (w_t.dtype != torch.uint8 or w_t.dim() != 1 or not w_t.is_contiguous()
+                or w_t.numel() != need):
+            raise ValueError(f"tiled weights must be a contiguous uint8 tensor of {need} bytes "
+                             f"(moe_tiled_weights_bytes({E}, {n_out}, {k_in}))")
     else:
         if weights.device != dev:
             raise ValueError(f"weights must be on {dev}, got {weights.device}")

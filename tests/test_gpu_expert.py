@@ -169,6 +169,12 @@ def test_grouped_gemm_rejects_bad_tensors():
         grouped_gemm(x, w, off[:2])
     with pytest.raises(MoeError):
         grouped_gemm(x[:, :60].contiguous(), w[:, :, :60].contiguous(), off)   # k_in % 8
+    t = tile_expert_weights(w)
+    bad = t._replace(data=t.data[:-16])                  # a tiled buffer of the wrong size
+    with pytest.raises(ValueError):
+        grouped_gemm(x, bad, off)
+    with pytest.raises(ValueError):
+        grouped_gemm(x, t._replace(n_out=128), off)
 
 
 def test_grouped_gemm_dsv3_full_size_sampled():
