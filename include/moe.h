@@ -297,9 +297,14 @@ int moe_dispatch_backward(moe_ctx *ctx, const void *d_grad_x_expert, const int32
  *   d_out       bf16 [max_rows][n_out]; must not overlap the inputs
  *   row_tile    rows per tile: 64, 128, or 0 for the library's choice
  *               (results do not depend on it)
+ *   weight_layout  MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_TILED; tiled weights
+ *               must come from moe_tile_expert_weights with the same
+ *               num_experts, n_out and k_in (the kernel trusts their size)
  * d_x_expert, d_weights and d_out must be 16-byte aligned, d_offsets
- * 4-byte aligned. 1 <= num_experts <= MOE_MAX_EXPERTS. Violations:
- * MOE_ERR_INVALID_ARG. */
+ * 4-byte aligned. 1 <= num_experts <= MOE_MAX_EXPERTS. A launch needs at
+ * most INT32_MAX workgroups (ceil(n_out/F) * (ceil(max_rows/row_tile) +
+ * num_experts), F = 128 row-major / 512 tiled features per workgroup).
+ * Violations: MOE_ERR_INVALID_ARG. */
 int moe_grouped_gemm(const void *d_x_expert, const void *d_weights, const int32_t *d_offsets,
                      int32_t num_experts, int64_t max_rows, int32_t k_in, int32_t n_out,
                      void *d_out, int32_t row_tile, int32_t weight_layout, void *stream);
