@@ -1,4 +1,6 @@
-"""MI355X (gfx950) MoE token routing layout, dispatch and combine.
+"""MI355X (gfx950) MoE token routing layout, dispatch and combine, their
+backward, and the expert step between them (a grouped GEMM driven by the
+device-side offsets).
 
 The compute lives in libmoe_layout.so (hand-written HIP kernels behind the C
 ABI of include/moe.h); this package is its thin Python binding.

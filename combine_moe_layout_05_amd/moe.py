@@ -1,4 +1,4 @@
-"""Python binding of the MoE layout / dispatch / combine C ABI.
+"""Python binding of the MoE layout / dispatch / combine / expert-step C ABI.
 
 Argument marshalling only: this module checks tensor placement, dtype and
 shape, passes raw device pointers and torch's current HIP stream to
