@@ -64,6 +64,8 @@ def parse_args():
                    help="1/0 forces combine's streaming loads on/off; -1 keeps the default")
     p.add_argument("--dispatch-block-waves", type=int, default=0)
     p.add_argument("--combine-block-waves", type=int, default=0)
+    p.add_argument("--combine-store-nontemporal", type=int, default=-1,
+                   help="1/0: streaming or ordinary stores of the combine output (-1: library default)")
     p.add_argument("--backward", type=int, default=0,
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--expert-iters", type=int, default=10,
@@ -252,7 +254,9 @@ def main() -> int:
     disp.set_tuning(args.dispatch_segments, args.combine_segments,
                     bool(args.dispatch_nontemporal) if args.dispatch_nontemporal >= 0 else None,
                     bool(args.combine_nontemporal) if args.combine_nontemporal >= 0 else None,
-                    args.dispatch_block_waves, args.combine_block_waves)
+                    args.dispatch_block_waves, args.combine_block_waves,
+                    bool(args.combine_store_nontemporal) if args.combine_store_nontemporal >= 0
+                    else None)
     tuning = disp.get_tuning()
     ntpr = w.ntpr
 
