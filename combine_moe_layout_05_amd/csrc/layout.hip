@@ -25,8 +25,9 @@
 //      slot index alone, so the result is deterministic under any skew.
 // Within a wavefront, slots with the same expert are found with a ballot per
 // expert-id bit (a lane's peers are the lanes whose id agrees on every bit);
-// the lowest peer updates the wavefront's LDS histogram once per group, so a
-// hot expert costs one LDS update per 64 slots, not 64.
+// the lowest peer updates the LDS histogram (the workgroup's when counting,
+// the wavefront's when ranking) once per group, so a hot expert costs one LDS
+// update per 64 slots, not 64.
 #include "moe_kernels.h"
 
 namespace moe {
