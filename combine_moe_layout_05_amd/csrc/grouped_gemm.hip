@@ -48,6 +48,8 @@
 #include "moe_kernels.h"
 #include "moe_lanes.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -84,6 +86,7 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
     constexpr int kThreads = WAVES * 64;
     constexpr int kFeatures = WAVES * 32;
     constexpr int U = BT / 32;                                        // 32-row sub-tiles
+    static_assert(U == 2 || U == 4, "row tile of 64 or 128");
     constexpr int UX = (BT * kStepChunks + kThreads - 1) / kThreads;  // row chunks per thread
     // Row buffer plus one dummy chunk per lane for threads past the tile.
     __shared__ v4i xs[2][BT * kStepChunks + 64];
@@ -189,122 +192,140 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
         xslot[j] = q < BT * kStepChunks ? r * kStepChunks + (c ^ swz(r))
                                         : BT * kStepChunks + lane;
     }
-    f32x16 acc[U];
+    // The tile's 32-row sub-tiles that hold rows of the segment (1..U): the
+    // loop is instantiated for each count and chosen once per workgroup, so
+    // short segments issue no matrix-core work for absent rows and the loop
+    // body stays branch-free.
+    auto run = [&](auto sub) {
+        constexpr int UU = decltype(sub)::value;
+        f32x16 acc[UU];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+        for (int u = 0; u < UU; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-    // One step: rows (and row-major weights) of the step, already in
-    // registers, to LDS; then the 4 x U matrix-core products.
-    auto mma_step = [&](int buf_id, const v4i (&wv)[4], const v4i (&xv)[UX], auto&& after_barrier) {
-        v4i* buf = xs[buf_id];
+        // One step: rows (and row-major weights) of the step, already in
+        // registers, to LDS; then the 4 x UU matrix-core products.
+        auto mma_step = [&](int buf_id, const v4i (&wv)[4], const v4i (&xv)[UX], auto&& after_barrier) {
+            v4i* buf = xs[buf_id];
 #pragma unroll
-        for (int j = 0; j < UX; ++j) buf[xslot[j]] = xv[j];
-        if constexpr (!TILED) {
+            for (int j = 0; j < UX; ++j) buf[xslot[j]] = xv[j];
+            if constexpr (!TILED) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wbuf[wslot[j]] = wv[j];
-        }
-        __syncthreads();
-        after_barrier();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8 a;
-            if constexpr (TILED)
-                a = as_bf16x8(wv[s]);
-            else
-                a = as_bf16x8(wbuf[i * kStepChunks + ((4 * h + s) ^ swz(i))]);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int r = u * 32 + i;
-                const bf16x8 b = as_bf16x8(buf[r * kStepChunks + ((4 * h + s) ^ swz(r))]);
-                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u], 0, 0, 0);
+                for (int j = 0; j < 4; ++j) wbuf[wslot[j]] = wv[j];
             }
-        }
-    };
+            __syncthreads();
+            after_barrier();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 a;
+                if constexpr (TILED)
+                    a = as_bf16x8(wv[s]);
+                else
+                    a = as_bf16x8(wbuf[i * kStepChunks + ((4 * h + s) ^ swz(i))]);
+#pragma unroll
+                for (int u = 0; u < UU; ++u) {
+                    const int r = u * 32 + i;
+                    const bf16x8 b = as_bf16x8(buf[r * kStepChunks + ((4 * h + s) ^ swz(r))]);
+                    acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u], 0, 0, 0);
+                }
+            }
+        };
 
-    const int32_t full = chunks / kStepChunks;
-    v4i wr[kStages][4];
-    v4i xr[kStages][UX];
-    auto load_w = [&](int32_t step, v4i (&dst)[4]) {
+        const int32_t full = chunks / kStepChunks;
+        v4i wr[kStages][4];
+        v4i xr[kStages][UX];
+        auto load_w = [&](int32_t step, v4i (&dst)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (TILED)
-                dst[j] = wt[(step * 4 + j) * 64];
-            else
-                dst[j] = wrow[j][step * kStepChunks];
-        }
-    };
-    auto load_x = [&](int32_t step, v4i (&dst)[UX]) {
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (TILED)
+                    dst[j] = wt[(step * 4 + j) * 64];
+                else
+                    dst[j] = wrow[j][step * kStepChunks];
+            }
+        };
+        auto load_x = [&](int32_t step, v4i (&dst)[UX]) {
 #pragma unroll
-        for (int j = 0; j < UX; ++j) dst[j] = xrow[j][step * kStepChunks];
-    };
-    // The loop body runs whole groups of kStages steps with no branch in it;
-    // the 0..kStages-1 steps left over run after it from the loaded ring.
-    int32_t done = 0;
-    if (full > 0) {
-#pragma unroll
-        for (int p = 0; p < kStages; ++p) {
-            load_x(min(p, full - 1), xr[p]);
-            load_w(min(p, full - 1), wr[p]);
-        }
-        int32_t s0 = 0;
-        for (; s0 + kStages <= full; s0 += kStages) {
+            for (int j = 0; j < UX; ++j) dst[j] = xrow[j][step * kStepChunks];
+        };
+        // The loop body runs whole groups of kStages steps with no branch in it;
+        // the 0..kStages-1 steps left over run after it from the loaded ring.
+        int32_t done = 0;
+        if (full > 0) {
 #pragma unroll
             for (int p = 0; p < kStages; ++p) {
-                const int32_t ahead = min(s0 + p + kStages, full - 1);
-                mma_step((s0 + p) & 1, wr[p], xr[p], [&] { load_x(ahead, xr[p]); });
-                load_w(ahead, wr[p]);
+                load_x(min(p, full - 1), xr[p]);
+                load_w(min(p, full - 1), wr[p]);
             }
-        }
+            int32_t s0 = 0;
+            for (; s0 + kStages <= full; s0 += kStages) {
 #pragma unroll
-        for (int p = 0; p < kStages - 1; ++p)
-            if (s0 + p < full) mma_step((s0 + p) & 1, wr[p], xr[p], [] {});
-        done = full;
-    }
-    // The last, partial step (k_in not a multiple of 64): row chunks past
-    // the row read as zero; row-major weight chunks too, tiled weights are
-    // zero there already.
-    if (done * kStepChunks < chunks) {
-        const int32_t c0 = done * kStepChunks;
-        const int32_t last = chunks - 1;
-        const v4i zero = {0, 0, 0, 0};
-        v4i wv[4], xv[UX];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (TILED) {
-                wv[j] = wt[(done * 4 + j) * 64];
-            } else {
-                const int32_t c = c0 + (lane & 7);
-                const v4i v = wrow[j][min(c, last) - (lane & 7)];
-                wv[j] = c <= last ? v : zero;
+                for (int p = 0; p < kStages; ++p) {
+                    const int32_t ahead = min(s0 + p + kStages, full - 1);
+                    mma_step((s0 + p) & 1, wr[p], xr[p], [&] { load_x(ahead, xr[p]); });
+                    load_w(ahead, wr[p]);
+                }
             }
-        }
 #pragma unroll
-        for (int j = 0; j < UX; ++j) {
-            const int32_t c = c0 + xc[j];
-            const v4i v = xrow[j][min(c, last) - xc[j]];
-            xv[j] = c <= last ? v : zero;
+            for (int p = 0; p < kStages - 1; ++p)
+                if (s0 + p < full) mma_step((s0 + p) & 1, wr[p], xr[p], [] {});
+            done = full;
         }
-        mma_step(done & 1, wv, xv, [] {});
-    }
+        // The last, partial step (k_in not a multiple of 64): row chunks past
+        // the row read as zero; row-major weight chunks too, tiled weights are
+        // zero there already.
+        if (done * kStepChunks < chunks) {
+            const int32_t c0 = done * kStepChunks;
+            const int32_t last = chunks - 1;
+            const v4i zero = {0, 0, 0, 0};
+            v4i wv[4], xv[UX];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (TILED) {
+                    wv[j] = wt[(done * 4 + j) * 64];
+                } else {
+                    const int32_t c = c0 + (lane & 7);
+                    const v4i v = wrow[j][min(c, last) - (lane & 7)];
+                    wv[j] = c <= last ? v : zero;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < UX; ++j) {
+                const int32_t c = c0 + xc[j];
+                const v4i v = xrow[j][min(c, last) - xc[j]];
+                xv[j] = c <= last ? v : zero;
+            }
+            mma_step(done & 1, wv, xv, [] {});
+        }
 
-    // acc[u][4q + t] is out[row u*32 + i][feature 32w + 8q + 4h + t].
+        // acc[u][4q + t] is out[row u*32 + i][feature 32w + 8q + 4h + t].
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int r = u * 32 + i;
-        if (r >= nrows) continue;
-        uint8_t* orow = out + (int64_t(row0 + r) * N) * 2;
+        for (int u = 0; u < UU; ++u) {
+            const int r = u * 32 + i;
+            if (r >= nrows) continue;
+            uint8_t* orow = out + (int64_t(row0 + r) * N) * 2;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int32_t col = f0 + wave * 32 + 8 * q + 4 * h;
-            if (col >= N) continue;
-            uint2 v;
-            v.x = f32_to_bf16_bits(acc[u][4 * q]) | (f32_to_bf16_bits(acc[u][4 * q + 1]) << 16);
-            v.y = f32_to_bf16_bits(acc[u][4 * q + 2]) | (f32_to_bf16_bits(acc[u][4 * q + 3]) << 16);
-            *reinterpret_cast<uint2*>(orow + int64_t(col) * 2) = v;
+            for (int q = 0; q < 4; ++q) {
+                const int32_t col = f0 + wave * 32 + 8 * q + 4 * h;
+                if (col >= N) continue;
+                uint2 v;
+                v.x = f32_to_bf16_bits(acc[u][4 * q]) | (f32_to_bf16_bits(acc[u][4 * q + 1]) << 16);
+                v.y = f32_to_bf16_bits(acc[u][4 * q + 2]) | (f32_to_bf16_bits(acc[u][4 * q + 3]) << 16);
+                *reinterpret_cast<uint2*>(orow + int64_t(col) * 2) = v;
+            }
         }
-    }
+    };
+    const int usub = (nrows + 31) / 32;
+    if (usub <= 1)
+        run(std::integral_constant<int, 1>{});
+    else if constexpr (U == 2)
+        run(std::integral_constant<int, 2>{});
+    else if (usub == 2)
+        run(std::integral_constant<int, 2>{});
+    else if (usub == 3)
+        run(std::integral_constant<int, 3>{});
+    else
+        run(std::integral_constant<int, U>{});
 }
 
 // Tiled weight layout: chunk ((((e * NB + b) * S + t) * 4 + s) * 64 + l) holds
