@@ -471,7 +471,8 @@ int moe_grouped_gemm(const void* d_x_expert, const void* d_weights, const int32_
     // Automatic tile: 128 rows once the average expert holds at least 64
     // rows at full capacity (fewer passes over each weight tile), else 64
     // (less padding for small segments). Measured on MI355X at 256 experts,
-    // 7168 -> 4096, 32768 rows of Zipf-skewed routing: 4.5 ms vs 4.9 ms.
+    // 7168 -> 4096, 32768 rows of Zipf-skewed routing: 3.5 ms vs 4.1 ms with
+    // tiled weights, 4.3 ms vs 4.9 ms row-major.
     if (row_tile == 0)
         row_tile = max_rows >= int64_t(64) * num_experts ? moe::kGemmRowTileLarge
                                                          : moe::kGemmRowTileSmall;

@@ -124,14 +124,18 @@ typedef struct moe_buffers_desc {
 typedef struct moe_ctx moe_ctx;
 
 /* Bytes of device workspace a context with this configuration needs.
- * Pure host. MOE_ERR_INVALID_ARG for an invalid configuration. */
+ * Pure host. MOE_ERR_CAPACITY when num_max_tokens_per_rank < 1,
+ * MOE_ERR_INVALID_ARG for any other invalid field or a NULL pointer. */
 int moe_workspace_bytes(const moe_config *cfg, size_t *bytes);
 
 /* Create a context over a caller-owned device workspace of `bytes` bytes
  * (>= moe_workspace_bytes, aligned to MOE_WORKSPACE_ALIGN). The buffers are
  * carved from it once, at fixed addresses; no call ever allocates or grows
  * them ([TT] "API design"). The caller keeps the workspace alive until
- * moe_destroy and frees it afterwards. Pure host; *out receives the context. */
+ * moe_destroy and frees it afterwards. Pure host; *out receives the context
+ * (NULL on error). Errors: as moe_workspace_bytes for the configuration;
+ * MOE_ERR_WORKSPACE for a short or misaligned workspace; MOE_ERR_INVALID_ARG
+ * for a NULL workspace or when the host-side context cannot be allocated. */
 int moe_create(const moe_config *cfg, void *d_workspace, size_t bytes, moe_ctx **out);
 
 /* Free the host-side context (not the workspace). NULL is accepted. */
