@@ -202,8 +202,10 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     // a 4096-token batch of 14 KiB rows launches 57344 wavefronts); dispatch
     // workgroups hold one token's whole row (its wavefronts then store
     // neighbouring pieces of the same rows together) and ordinary stores;
-    // combine uses 4-wavefront workgroups and streaming loads (the
-    // expert-output rows are read exactly once).
+    // combine uses 16-wavefront workgroups (against 4: 3-5 % faster at the
+    // 32k-token, 8192-token and 2048-token shapes, equal at 4096 tokens of
+    // 7168) and streaming loads (the expert-output rows are read exactly
+    // once).
     int32_t seg = (c->chunks + 63) / 64;
     if (seg > moe::kMaxSegments) seg = moe::kMaxSegments;
     const int32_t seg_eff =
@@ -213,7 +215,7 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     c->tuning.dispatch_nontemporal = 0;
     c->tuning.combine_nontemporal = 1;
     c->tuning.dispatch_block_waves = seg_eff >= 4 ? seg_eff : moe::kMaxBlockWaves;
-    c->tuning.combine_block_waves = 4;
+    c->tuning.combine_block_waves = moe::kMaxBlockWaves;
     // Stream y past the caches when the whole output buffer exceeds the
     // last-level cache: it cannot stay cached for its consumer, and ordinary
     // stores would leave dirty lines to be written back during later kernels.

@@ -253,7 +253,7 @@ def test_tuning_roundtrip_and_limits(lib):
     assert 1 <= t.dispatch_segments <= 16 and 1 <= t.combine_segments <= 16
     assert 1 <= t.dispatch_block_waves <= 16 and 1 <= t.combine_block_waves <= 16
     # 7168 bf16 = 896 chunks: 14 one-chunk segments; a dispatch workgroup per token row
-    assert (t.dispatch_segments, t.dispatch_block_waves, t.combine_block_waves) == (14, 14, 4)
+    assert (t.dispatch_segments, t.dispatch_block_waves, t.combine_block_waves) == (14, 14, 16)
     assert t.combine_store_nontemporal == 0          # 58.7 MB output: stays cacheable
     assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1))) == L.MOE_OK
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
