@@ -5,7 +5,9 @@ One step is one pass of the whole path over one synthetic batch already
 resident in HBM: moe_layout, moe_dispatch, the identity expert (the combine
 reads the dispatched buffer), moe_combine. The default workload is the
 DeepSeek-V3-shaped layer (T=4096, D=7168, E=256, top-8, bf16, Zipf(1.1)
-routing). Prints one JSON line.
+routing). Prints one JSON line. `value` and `ms_per_step` time K plain
+steps; the per-kernel times (and the roofline of the dominant kernel) come
+from a second pass of K steps with HIP events around each call.
 
 The line also carries, under "expert_step", the expert step between dispatch
 and combine (moe_grouped_gemm: one linear map per expert driven by the
@@ -54,6 +56,8 @@ def parse_args():
                    help="iterations of the cache-flushed per-kernel measurement (0 = skip)")
     p.add_argument("--graph-replays", type=int, default=20,
                    help="timed replays of the step captured in a hipGraph (0 = skip)")
+    p.add_argument("--fused-steps", type=int, default=50,
+                   help="also time the step with moe_layout_dispatch (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget of the oracle CPU baseline (0 = skip)")
     p.add_argument("--dispatch-segments", type=int, default=0)
@@ -278,15 +282,26 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
+    # The timed region: K steps exactly as a caller runs them, no
+    # instrumentation. The per-kernel times come from a second pass of K
+    # steps with HIP events recorded around each call on the launch stream
+    # (the event records add a few microseconds per step, so that pass is
+    # reported separately and does not set `value`).
     K = args.steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     log(f"timed {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    log(f"{K} steps with per-kernel events")
+    t_ev = time.perf_counter()
     for i in range(K):
         step(events[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    ms_per_step_events = (time.perf_counter() - t_ev) * 1e3 / K
     lay_ms = [e[0].elapsed_time(e[1]) for e in events]
     dis_ms = [e[1].elapsed_time(e[2]) for e in events]
     com_ms = [e[2].elapsed_time(e[3]) for e in events]
@@ -324,6 +339,36 @@ def main() -> int:
         graph_us = (time.perf_counter() - t_g) * 1e6 / args.graph_replays
         del g
         log(f"graph replay {graph_us:.1f} us per step")
+
+    # The same step with the layout fused into dispatch (moe_layout_dispatch:
+    # two launches instead of three), timed the same way; reported beside the
+    # separate calls, which remain the measured step.
+    fused = None
+    if args.fused_steps > 0:
+        log(f"fused layout+dispatch step, {args.fused_steps} timed steps")
+
+        def fused_step():
+            lay, dsp = disp.layout_dispatch(x, s, ids, num_tokens_per_rank=ntpr)
+            disp.combine(dsp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
+
+        for _ in range(args.warmup):
+            fused_step()
+        torch.cuda.synchronize()
+        t_f = time.perf_counter()
+        for _ in range(args.fused_steps):
+            fused_step()
+        torch.cuda.synchronize()
+        fused_us = (time.perf_counter() - t_f) * 1e6 / args.fused_steps
+        fused = {"step_us": round(fused_us, 2),
+                 "vs_separate_step": round(fused_us / (ms_per_step * 1e3), 4)}
+        # the separate calls once more, right after, against drift
+        t_s = time.perf_counter()
+        for _ in range(args.fused_steps):
+            step()
+        torch.cuda.synchronize()
+        fused["separate_step_us_after"] = round((time.perf_counter() - t_s) * 1e6 /
+                                                args.fused_steps, 2)
+        log(f"fused step {fused_us:.1f} us")
 
     # Cold-cache per-kernel times: a 1 GiB read evicts L2 and the MALL
     # before each timed kernel (outside the timed interval); a read leaves
@@ -442,6 +487,8 @@ def main() -> int:
         },
         "cold_cache": cold,
         "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
+        "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
+        "fused_layout_dispatch": fused,
         "backward": backward,
         "expert_step": expert,
     }

@@ -64,6 +64,7 @@ SIGNATURES = {
     "moe_dispatch": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "moe_combine": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
     "moe_dispatch_scaled": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+    "moe_layout_dispatch": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "moe_topk_from_routing_map": (_int, [_vp, _vp, _vp, _i32, _vp, C.POINTER(_vp),
                                          C.POINTER(_vp), C.POINTER(_vp)]),
     "moe_combine_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp),

@@ -238,6 +238,136 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
     }
 }
 
+// Completion counters of the fused count launch, one per context and device:
+// zero when the code object loads, and the last workgroup of every launch
+// puts its counter back to zero.
+__device__ uint32_t g_fused_done[kFusedCounterSlots];
+
+// Count launch of the layout fused into dispatch. Every workgroup histograms
+// its tile (as layout_count_kernel) and marks its tile's padding slots as
+// routing nowhere. The last workgroup to finish then turns the histograms,
+// in place, into each tile's first row per expert: offsets[e] plus the
+// count of expert e in all earlier tiles; it also writes counts and
+// offsets. Nothing waits: the workgroup that sees the counter reach
+// gridDim.x - 1 is the one that continues. Thread (quad q, slice sl) owns
+// experts 4q..4q+3 over the contiguous tile range of slice sl, summed with
+// 16-byte loads; slice sums go through LDS.
+template <int R>
+__global__ __launch_bounds__(kLayoutThreads)
+void layout_count_scan_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t nslots,
+                              int32_t E, int32_t E4, int bits, int32_t tiles, int32_t slot,
+                              int32_t* __restrict__ block_hist, int32_t* __restrict__ counts,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ row_map) {
+    __shared__ int32_t hist[kMaxExperts];
+    __shared__ int32_t part[kMaxExperts];   // slice sums, [S][E4] (S * E4 <= 4 * kLayoutThreads)
+    __shared__ int32_t first[kMaxExperts];  // offsets, then slice bases
+    __shared__ int32_t wave_sum[kLayoutWaves];
+    __shared__ int last;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    constexpr int kTile = kLayoutThreads * R;
+
+    if (static_cast<int32_t>(blockIdx.x) < tiles) {
+        for (int e = tid; e < E4; e += kLayoutThreads) hist[e] = 0;
+        __syncthreads();
+        const int64_t base = int64_t(blockIdx.x) * kTile + wave * (64 * R);
+        int32_t ex[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
+        const uint64_t below = lanes_below();
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const bool valid = ex[j] >= 0;
+            const uint64_t peers = peer_mask(ex[j], valid, bits);
+            if (valid && (peers & below) == 0) atomicAdd(&hist[ex[j]], __popcll(peers));
+        }
+        __syncthreads();
+        int32_t* out = block_hist + int64_t(blockIdx.x) * E4;
+        for (int e = tid; e < E4; e += kLayoutThreads) out[e] = hist[e];
+        // Padding slots of this tile (t >= T) route nowhere.
+        const int64_t t0 = int64_t(blockIdx.x) * kTile;
+        const int64_t t1 = t0 + kTile < nslots ? t0 + kTile : nslots;
+        for (int64_t i = (t0 > nvalid ? t0 : nvalid) + tid; i < t1; i += kLayoutThreads)
+            row_map[i] = -1;
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last = atomicAdd(&g_fused_done[slot], 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+
+    const int quads = E4 / 4;
+    int S = kLayoutThreads / quads;
+    if (S > kMaxSlices) S = kMaxSlices;
+    const int q = tid % quads;
+    const int sl = tid / quads;
+    const int32_t per = (tiles + S - 1) / S;
+    const int32_t b_lo = sl < S ? min(sl * per, tiles) : tiles;
+    const int32_t b_hi = min(b_lo + per, tiles);
+    v4i* h = reinterpret_cast<v4i*>(block_hist) + q;
+    if (sl < S) {
+        v4i sum = {0, 0, 0, 0};
+#pragma unroll 8
+        for (int32_t b = b_lo; b < b_hi; ++b) sum += h[int64_t(b) * quads];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[sl * E4 + 4 * q + j] = sum[j];
+    }
+    __syncthreads();
+
+    // Totals per expert and their exclusive scan (thread order = expert order).
+    const int e0 = tid * kExpertsPerThread;
+    int32_t tot[kExpertsPerThread];
+    int32_t mine_sum = 0;
+#pragma unroll
+    for (int j = 0; j < kExpertsPerThread; ++j) {
+        tot[j] = 0;
+        if (e0 + j < E4)
+            for (int k = 0; k < S; ++k) tot[j] += part[k * E4 + e0 + j];
+        mine_sum += tot[j];
+    }
+    int32_t incl = mine_sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t up = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += up;
+    }
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - mine_sum;
+    for (int w = 0; w < wave; ++w) run += wave_sum[w];
+#pragma unroll
+    for (int j = 0; j < kExpertsPerThread; ++j) {
+        const int e = e0 + j;
+        if (e < E4) first[e] = run;
+        if (e < E) {
+            counts[e] = tot[j];
+            offsets[e] = run;
+        }
+        run += tot[j];
+    }
+    if (tid == kLayoutThreads - 1) offsets[E] = run;
+    __syncthreads();
+
+    // Each tile's first row per expert, written over its histogram.
+    if (sl < S) {
+        v4i r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            r[j] = first[4 * q + j];
+            for (int k = 0; k < sl; ++k) r[j] += part[k * E4 + 4 * q + j];
+        }
+#pragma unroll 8
+        for (int32_t b = b_lo; b < b_hi; ++b) {
+            const v4i v = h[int64_t(b) * quads];
+            h[int64_t(b) * quads] = r;
+            r += v;
+        }
+    }
+    if (tid == 0) atomicExch(&g_fused_done[slot], 0u);
+}
+
 template <int R>
 hipError_t launch_r(const LayoutArgs& a, hipStream_t stream) {
     const int64_t tiles = layout_tiles(a.nslots, R);
@@ -259,7 +389,30 @@ hipError_t launch_r(const LayoutArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int R>
+hipError_t launch_count_scan_r(const LayoutArgs& a, int32_t slot, hipStream_t stream) {
+    const int64_t tiles = layout_tiles(a.nslots, R);
+    // At least one workgroup, so counts and offsets are written even for an
+    // empty capacity.
+    const uint32_t grid = static_cast<uint32_t>(tiles > 0 ? tiles : 1);
+    hipLaunchKernelGGL(layout_count_scan_kernel<R>, dim3(grid), dim3(kLayoutThreads), 0, stream,
+                       a.ids, a.nvalid, a.nslots, a.E, padded_experts(a.E), expert_bits(a.E),
+                       static_cast<int32_t>(tiles), slot, a.block_hist, a.counts, a.offsets,
+                       a.row_map);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_layout_count_scan(const LayoutArgs& a, int32_t counter_slot, int32_t* tile_slots,
+                                    hipStream_t stream) {
+    if (counter_slot < 0 || counter_slot >= kFusedCounterSlots) return hipErrorInvalidValue;
+    const int R = layout_slots_per_lane(a.nslots);
+    *tile_slots = kLayoutThreads * R;
+    return R == kLayoutMinSlotsPerLane
+               ? launch_count_scan_r<kLayoutMinSlotsPerLane>(a, counter_slot, stream)
+               : launch_count_scan_r<kLayoutMaxSlotsPerLane>(a, counter_slot, stream);
+}
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     return layout_slots_per_lane(a.nslots) == kLayoutMinSlotsPerLane

@@ -17,6 +17,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "moe.h"
@@ -33,6 +34,8 @@ struct moe_ctx {
     int32_t layout_T;
     int64_t layout_ntpr4;
     moe_tuning tuning;
+    // Completion-counter slot of moe_layout_dispatch (-1: none was free).
+    int32_t counter_slot;
 };
 
 namespace {
@@ -99,6 +102,28 @@ void plan(const moe_config* cfg, moe_buffers_desc* d) {
     d->workspace_bytes = at;
 }
 
+// Counter slots of the fused layout+dispatch, shared by all contexts of the
+// process (the counters themselves live in device memory, one array per
+// device). A context holds its slot from create to destroy.
+std::mutex g_slot_mutex;
+bool g_slot_used[moe::kFusedCounterSlots];
+
+int32_t take_counter_slot() {
+    std::lock_guard<std::mutex> lock(g_slot_mutex);
+    for (int32_t i = 0; i < moe::kFusedCounterSlots; ++i)
+        if (!g_slot_used[i]) {
+            g_slot_used[i] = true;
+            return i;
+        }
+    return -1;
+}
+
+void release_counter_slot(int32_t slot) {
+    if (slot < 0) return;
+    std::lock_guard<std::mutex> lock(g_slot_mutex);
+    g_slot_used[slot] = false;
+}
+
 template <typename T>
 T* at(const moe_ctx* c, int64_t off) {
     return reinterpret_cast<T*>(c->ws + off);
@@ -162,7 +187,8 @@ const char* moe_strerror(int status) {
         case MOE_ERR_STATE:
             return "dispatch/combine does not match the context's latest layout";
         case MOE_ERR_UNSUPPORTED:
-            return "backward call on a context created without MOE_FLAG_BACKWARD";
+            return "backward call on a context created without MOE_FLAG_BACKWARD, or fused "
+                   "layout+dispatch on a context without a counter slot";
         default: return "unknown status";
     }
 }
@@ -197,6 +223,7 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     c->has_layout = false;
     c->layout_T = -1;
     c->layout_ntpr4 = -1;
+    c->counter_slot = take_counter_slot();
     // Defaults from measurement on MI355X: one 16-byte chunk per lane per
     // wavefront (a row of up to 16 KiB becomes up to 16 wavefront items, so
     // a 4096-token batch of 14 KiB rows launches 57344 wavefronts); dispatch
@@ -225,6 +252,7 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
 }
 
 int moe_destroy(moe_ctx* ctx) {
+    if (ctx) release_counter_slot(ctx->counter_slot);
     delete ctx;
     return MOE_OK;
 }
@@ -259,16 +287,11 @@ int moe_get_tuning(const moe_ctx* ctx, moe_tuning* out) {
     return MOE_OK;
 }
 
-int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
-               void* stream) {
-    if (!ctx) return MOE_ERR_INVALID_ARG;
-    int64_t ntpr4 = 0;
-    const int st = check_call(ctx, T, ntpr, &ntpr4);
-    if (st != MOE_OK) return st;
-    if (T > 0 && !d_topk_ids) return MOE_ERR_INVALID_ARG;
+static moe::LayoutArgs layout_args(const moe_ctx* ctx, const int32_t* d_ids, int32_t T,
+                                   int64_t ntpr4) {
     const int64_t K = ctx->cfg.topk;
     moe::LayoutArgs a;
-    a.ids = d_topk_ids;
+    a.ids = d_ids;
     a.nvalid = int64_t(T) * K;
     a.nslots = ntpr4 * K;
     a.E = ctx->cfg.num_experts;
@@ -277,7 +300,38 @@ int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
     a.offsets = at<int32_t>(ctx, ctx->desc.offsets);
     a.row_map = at<int32_t>(ctx, ctx->desc.row_map);
     a.src_map = at<int32_t>(ctx, ctx->desc.src_map);
-    if (moe::launch_layout(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return a;
+}
+
+static moe::DispatchArgs dispatch_args(const moe_ctx* ctx, const void* d_x, const float* d_scores,
+                                       int32_t T, bool scaled) {
+    moe::DispatchArgs a;
+    a.x = d_x;
+    a.scores = d_scores;
+    a.row_map = at<int32_t>(ctx, ctx->desc.row_map);
+    a.T = T;
+    a.K = ctx->cfg.topk;
+    a.chunks = ctx->chunks;
+    a.max_rows = ctx->desc.max_rows;
+    a.x_e = at<void>(ctx, ctx->desc.x_e);
+    a.s_e = at<float>(ctx, ctx->desc.s_e);
+    a.segments = ctx->tuning.dispatch_segments;
+    a.block_waves = ctx->tuning.dispatch_block_waves;
+    a.nontemporal = ctx->tuning.dispatch_nontemporal != 0;
+    a.scaled = scaled;
+    a.bf16 = ctx->cfg.dtype == MOE_BF16;
+    return a;
+}
+
+int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
+               void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    int64_t ntpr4 = 0;
+    const int st = check_call(ctx, T, ntpr, &ntpr4);
+    if (st != MOE_OK) return st;
+    if (T > 0 && !d_topk_ids) return MOE_ERR_INVALID_ARG;
+    if (moe::launch_layout(layout_args(ctx, d_topk_ids, T, ntpr4),
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     ctx->has_layout = true;
     ctx->layout_T = T;
@@ -296,23 +350,30 @@ static int dispatch_impl(moe_ctx* ctx, const void* d_x, const float* d_scores,
     if (T > 0 && (!d_x || !d_scores || !d_ids)) return MOE_ERR_INVALID_ARG;
     if (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4)
         return MOE_ERR_STATE;
-    moe::DispatchArgs a;
-    a.x = d_x;
-    a.scores = d_scores;
-    a.row_map = at<int32_t>(ctx, ctx->desc.row_map);
-    a.T = T;
-    a.K = ctx->cfg.topk;
-    a.chunks = ctx->chunks;
-    a.max_rows = ctx->desc.max_rows;
-    a.x_e = at<void>(ctx, ctx->desc.x_e);
-    a.s_e = at<float>(ctx, ctx->desc.s_e);
-    a.segments = ctx->tuning.dispatch_segments;
-    a.block_waves = ctx->tuning.dispatch_block_waves;
-    a.nontemporal = ctx->tuning.dispatch_nontemporal != 0;
-    a.scaled = scaled;
-    a.bf16 = ctx->cfg.dtype == MOE_BF16;
-    if (moe::launch_dispatch(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (moe::launch_dispatch(dispatch_args(ctx, d_x, d_scores, T, scaled),
+                             static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_layout_dispatch(moe_ctx* ctx, const void* d_x, const float* d_scores,
+                        const int32_t* d_topk_ids, int32_t T, int32_t ntpr, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    int64_t ntpr4 = 0;
+    const int st = check_call(ctx, T, ntpr, &ntpr4);
+    if (st != MOE_OK) return st;
+    if (ctx->counter_slot < 0) return MOE_ERR_UNSUPPORTED;
+    if (T > 0 && (!d_x || !d_scores || !d_topk_ids)) return MOE_ERR_INVALID_ARG;
+    moe::FusedLayoutDispatchArgs a;
+    a.layout = layout_args(ctx, d_topk_ids, T, ntpr4);
+    a.dispatch = dispatch_args(ctx, d_x, d_scores, T, false);
+    a.ids = d_topk_ids;
+    a.counter_slot = ctx->counter_slot;
+    if (moe::launch_layout_dispatch(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    ctx->has_layout = true;
+    ctx->layout_T = T;
+    ctx->layout_ntpr4 = ntpr4;
     return MOE_OK;
 }
 

@@ -98,6 +98,26 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
+// Layout fused into dispatch, two launches instead of three. The count
+// launch's last workgroup to finish (found with a per-context completion
+// counter, kept in a static device array so it starts at zero) turns the
+// tile histograms in block_hist into each tile's first row per expert and
+// writes counts and offsets; dispatch then ranks each of its tokens' slots
+// among the earlier slots of the same tile, writes row_map and src_map, and
+// copies the rows. Results equal moe_layout followed by moe_dispatch.
+constexpr int kFusedCounterSlots = 1024;
+struct FusedLayoutDispatchArgs {
+    LayoutArgs layout;      // block_hist ends up holding each tile's first rows
+    DispatchArgs dispatch;  // row_map is written here, not read
+    const int32_t* ids;     // [T][K]
+    int32_t counter_slot;   // 0 .. kFusedCounterSlots-1, one per context
+};
+hipError_t launch_layout_dispatch(const FusedLayoutDispatchArgs& a, hipStream_t stream);
+// The count launch of the fused path (defined with the layout kernels);
+// tile_slots receives the tile size it used.
+hipError_t launch_layout_count_scan(const LayoutArgs& a, int32_t counter_slot, int32_t* tile_slots,
+                                    hipStream_t stream);
+
 struct CombineArgs {
     const void* y_e;        // [>= total][row_bytes]
     const int32_t* row_map; // [T][K]

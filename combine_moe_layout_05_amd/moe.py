@@ -261,6 +261,27 @@ class MoeDispatcher:
         rows = round_up4(ntpr) * self.topk
         return Dispatched(self.x_e[:rows], self.s_e[:rows])
 
+    def layout_dispatch(self, x_TD: torch.Tensor, topk_scores_TK: torch.Tensor,
+                        topk_expert_ids_TK: torch.Tensor, *,
+                        num_tokens_per_rank: Optional[int] = None):
+        """layout() then dispatch() in two launches instead of three
+        (moe_layout_dispatch); same results bit for bit. Returns (Layout,
+        Dispatched)."""
+        x = self._dev(x_TD, "x_TD", self.dtype, self.hidden)
+        T = x.shape[0]
+        s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
+        ids = self._dev(topk_expert_ids_TK, "topk_expert_ids_TK", torch.int32, self.topk)
+        if s.shape[0] != T or ids.shape[0] != T:
+            raise ValueError("x_TD, topk_scores_TK and topk_expert_ids_TK need the same T")
+        ntpr = self._ntpr(T, num_tokens_per_rank)
+        L.check(self._lib.moe_layout_dispatch(self._ctx, x.data_ptr(), s.data_ptr(),
+                                              ids.data_ptr(), T, ntpr, _stream(self.device)),
+                "moe_layout_dispatch")
+        n4 = round_up4(ntpr)
+        rows = n4 * self.topk
+        return (Layout(self.counts, self.offsets, self.row_map[:n4]),
+                Dispatched(self.x_e[:rows], self.s_e[:rows]))
+
     def topk_from_routing_map(self, routing_map_TE: torch.Tensor, probs_TE: torch.Tensor):
         """(ids [T, K], scores [T, K], n_experts [T]) views: the top-k form of
         a boolean routing map with probabilities (experts in ascending order,

@@ -57,7 +57,8 @@ extern "C" {
 #define MOE_ERR_WORKSPACE   (-3) /* workspace too small or misaligned */
 #define MOE_ERR_HIP         (-4) /* a HIP launch reported an error */
 #define MOE_ERR_STATE       (-5) /* dispatch/combine without a matching layout */
-#define MOE_ERR_UNSUPPORTED (-6) /* backward call on a context without MOE_FLAG_BACKWARD */
+#define MOE_ERR_UNSUPPORTED (-6) /* backward call without MOE_FLAG_BACKWARD; moe_layout_dispatch
+                                    on a context that got no counter slot */
 
 /* moe_config.flags */
 #define MOE_FLAG_BACKWARD   1    /* also carve the backward buffers g_e, g_s, g_x */
@@ -175,6 +176,27 @@ int moe_layout(moe_ctx *ctx, const int32_t *d_topk_ids, int32_t T,
 int moe_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
                  const int32_t *d_topk_ids, const int32_t *d_counts, int32_t T,
                  int32_t num_tokens_per_rank, void *stream);
+
+/* moe_layout followed by moe_dispatch in two launches instead of three, with
+ * the same results bit for bit: counts, offsets, row_map, src_map, x_e and
+ * s_e exactly as those two calls write them ([TT] "Backend behavior": the
+ * fused-permute output is sized from the current capacity; [UC] "Internode"
+ * 2 and 3: the counts and the total stay on the device). The count launch's
+ * last workgroup to finish scans the per-tile expert histograms into each
+ * tile's first row per expert; the dispatch workgroups rank their tokens'
+ * slots within their tile, record the rows and copy the hidden states. No
+ * workgroup waits on another. The last workgroup is found with a completion
+ * counter that lives in a static device array (one slot per context, taken
+ * at moe_create and given back at moe_destroy; MOE_ERR_UNSUPPORTED when all
+ * 1024 slots were taken) and is back at zero after every launch, so the call
+ * is graph-capturable like the others. Arguments and capacity checks are
+ * those of moe_layout plus moe_dispatch (no d_counts: the context's own is
+ * used). Records the context's current layout like moe_layout, so
+ * moe_combine follows as usual. Two calls on one context must not overlap
+ * (as for every entry point); destroy a context only after its work ended. */
+int moe_layout_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
+                        const int32_t *d_topk_ids, int32_t T, int32_t num_tokens_per_rank,
+                        void *stream);
 
 /* Dispatch with the scores applied (the weighting moved from the combine to
  * the dispatch; [NA] "Fix": the dispatcher's inputs are hidden states,

@@ -50,6 +50,12 @@ static void one_config(int32_t nmax, int32_t D, int32_t E, int32_t K, int32_t dt
         EXPECT(moe_dispatch_scaled(ctx, p, static_cast<const float*>(p),
                                    static_cast<const int32_t*>(p), counts, T, ntpr,
                                    nullptr) == MOE_OK);
+        EXPECT(moe_layout_dispatch(ctx, p, static_cast<const float*>(p),
+                                   static_cast<const int32_t*>(p), T, ntpr, nullptr) == MOE_OK);
+        if (T > 0)
+            EXPECT(moe_layout_dispatch(ctx, nullptr, static_cast<const float*>(p),
+                                       static_cast<const int32_t*>(p), T, ntpr, nullptr) ==
+                   MOE_ERR_INVALID_ARG);
         void* y = nullptr;
         EXPECT(moe_combine(ctx, p, row_map, static_cast<const float*>(p), T, ntpr, nullptr, &y) ==
                MOE_OK);
@@ -75,6 +81,12 @@ static void one_config(int32_t nmax, int32_t D, int32_t E, int32_t K, int32_t dt
            MOE_ERR_CAPACITY);
     EXPECT(moe_layout(ctx, static_cast<const int32_t*>(p), -1, nmax, nullptr) ==
            MOE_ERR_CAPACITY);
+    EXPECT(moe_layout_dispatch(ctx, p, static_cast<const float*>(p),
+                               static_cast<const int32_t*>(p), nmax + 1, nmax + 1, nullptr) ==
+           MOE_ERR_CAPACITY);
+    EXPECT(moe_layout_dispatch(nullptr, p, static_cast<const float*>(p),
+                               static_cast<const int32_t*>(p), 0, 0, nullptr) ==
+           MOE_ERR_INVALID_ARG);
     EXPECT(moe_dispatch(ctx, p, static_cast<const float*>(p), static_cast<const int32_t*>(p),
                         counts + 1, 0, nmax, nullptr) != MOE_OK);
     moe_tuning t;

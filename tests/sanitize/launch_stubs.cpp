@@ -31,6 +31,17 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t) {
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_layout_dispatch(const FusedLayoutDispatchArgs& a, hipStream_t) {
+    require(a.layout.E >= 1 && a.layout.nvalid >= 0 && a.layout.nslots >= a.layout.nvalid &&
+                a.counter_slot >= 0 && a.counter_slot < kFusedCounterSlots &&
+                a.dispatch.T >= 0 && a.dispatch.K >= 1 && a.dispatch.chunks >= 1 &&
+                a.dispatch.segments >= 1 && a.dispatch.block_waves >= 1 &&
+                a.dispatch.block_waves <= kMaxBlockWaves &&
+                a.layout.nvalid == int64_t(a.dispatch.T) * a.dispatch.K && a.ids == a.layout.ids,
+            "fused layout+dispatch shape");
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_combine(const CombineArgs& a, hipStream_t) {
     require(a.T >= 0 && a.K >= 1 && a.chunks >= 1 && a.segments >= 1 && a.block_waves >= 1 &&
                 a.block_waves <= kMaxBlockWaves && a.row_limit >= 0,

@@ -209,6 +209,46 @@ def test_variant_calls_reject_bad_arguments(lib):
     lib.moe_destroy(ctx)
 
 
+def test_fused_layout_dispatch_rejects_bad_arguments(lib):
+    ctx, d, _ = _ctx(lib, _cfg(4096, 2048, 128, 8, L.MOE_BF16))
+    p = 1 << 41
+    assert lib.moe_layout_dispatch(ctx, p, p, p, 4097, 4097, None) == L.MOE_ERR_CAPACITY
+    assert lib.moe_layout_dispatch(ctx, p, p, p, 9, 8, None) == L.MOE_ERR_CAPACITY
+    assert lib.moe_layout_dispatch(ctx, p, p, p, -1, 8, None) == L.MOE_ERR_CAPACITY
+    for bad in ((None, p, p), (p, None, p), (p, p, None)):
+        assert lib.moe_layout_dispatch(ctx, *bad, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_layout_dispatch(None, p, p, p, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    lib.moe_destroy(ctx)
+
+
+def test_fused_counter_slots_run_out_and_come_back(lib):
+    # Each context holds one of 1024 completion-counter slots from create to
+    # destroy. The slot is checked before the pointers, so a call with a NULL
+    # x tells the two cases apart without enqueueing anything: no slot gives
+    # MOE_ERR_UNSUPPORTED, a slot MOE_ERR_INVALID_ARG.
+    p = 1 << 41
+    cfg = _cfg(64, 128, 8, 2, L.MOE_F32)
+    made = []
+    try:
+        for _ in range(1100):
+            c, _, _ = _ctx(lib, cfg)
+            made.append(c)
+            if lib.moe_layout_dispatch(c, None, p, p, 5, 8, None) == L.MOE_ERR_UNSUPPORTED:
+                break
+        else:
+            pytest.fail("contexts never ran out of counter slots")
+        assert len(made) <= 1025
+        first = made.pop(0)
+        assert lib.moe_layout_dispatch(first, None, p, p, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+        lib.moe_destroy(first)                      # its slot becomes free again
+        c, _, _ = _ctx(lib, cfg)
+        made.append(c)
+        assert lib.moe_layout_dispatch(c, None, p, p, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    finally:
+        for c in made:
+            lib.moe_destroy(c)
+
+
 def test_grouped_gemm_rejects_bad_arguments(lib):
     p = 1 << 41                                   # 16-byte aligned, never dereferenced
     ok = dict(x=p, w=p, off=p, E=256, rows=32768, k=7168, n=4096, out=p, tile=0, lay=0)
