@@ -13,13 +13,14 @@
 // expert's segment), F = 32 per wavefront. Within an expert, tiles go in
 // blocks of up to 8 row tiles: all feature tiles of a block, each with the
 // block's row tiles fastest. Workgroups are dealt to the 8 XCDs round-robin,
-// so each XCD is given a contiguous run of tile numbers; the workgroups an
-// XCD runs at once then cover a few row tiles x feature tiles of one expert,
+// so each XCD is given a contiguous run of tile numbers (or, for long
+// segments, every eighth chunk of 16 tile numbers); the workgroups an XCD
+// runs at once then cover a few row tiles x feature tiles of one expert,
 // which share each weight tile and each row tile through that XCD's L2 (with
 // a plain feature-major order a large expert re-fetches its rows once per
 // feature tile). The grid covers the most tiles any routing can need,
-// ceil(max_rows / BT) + E row tiles per feature tile (rounded up to a
-// multiple of 8); wavefront 0 of each workgroup finds its tile from the
+// ceil(max_rows / BT) + E row tiles per feature tile (rounded up to whole
+// chunks per XCD); wavefront 0 of each workgroup finds its tile from the
 // offsets (a scan of the per-expert tile counts over the 64 lanes) and
 // workgroups without a tile exit.
 //
@@ -82,7 +83,8 @@ template <int BT, int WAVES, bool TILED>
 __global__ __launch_bounds__(WAVES * 64)
 void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
                          const int32_t* __restrict__ offsets, int32_t E, int32_t max_rows,
-                         int32_t chunks, int32_t N, int32_t ftiles, uint8_t* __restrict__ out) {
+                         int32_t chunks, int32_t N, int32_t ftiles, int32_t xcd_chunk,
+                         uint8_t* __restrict__ out) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kFeatures = WAVES * 32;
     constexpr int U = BT / 32;                                        // 32-row sub-tiles
@@ -115,12 +117,21 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
         // Workgroup b runs on XCD b % kXcds (round-robin dispatch); XCD x
         // takes the tile run [x * run, (x + 1) * run).
         const int64_t total = __shfl(incl, 63, 64);
-        const int64_t run = (total + kXcds - 1) / kXcds;
+        // Contiguous runs: XCD x takes [x * run, (x + 1) * run). Chunks: XCD x
+        // takes chunks x, x + 8, x + 16, ... of xcd_chunk tiles each (the grid
+        // holds whole chunks per XCD, so every tile number is dealt).
         const int64_t idx = blockIdx.x / kXcds;
-        const int64_t u = (blockIdx.x % kXcds) * run + idx;
-        if (lane == 0 && (idx >= run || u >= total)) info[0] = -1;
+        const int64_t x = blockIdx.x % kXcds;
+        int64_t u;
+        if (xcd_chunk > 0) {
+            u = ((idx / xcd_chunk) * kXcds + x) * xcd_chunk + idx % xcd_chunk;
+        } else {
+            const int64_t run = (total + kXcds - 1) / kXcds;
+            u = idx < run ? x * run + idx : total;
+        }
+        if (lane == 0 && u >= total) info[0] = -1;
         int64_t base = incl - local;
-        if (idx < run && u >= base && u < incl) {
+        if (u >= base && u < incl) {
             for (int e = e_lo; e < e_hi; ++e) {
                 int32_t s0, s1;
                 segment(offsets, e, max_rows, s0, s1);
@@ -360,7 +371,7 @@ hipError_t launch_bt(const GroupedGemmArgs& a, hipStream_t stream) {
                        static_cast<const v4i*>(a.w), a.offsets, a.E,
                        static_cast<int32_t>(a.max_rows), a.Kd / 8, a.N,
                        static_cast<int32_t>((a.N + WAVES * 32 - 1) / (WAVES * 32)),
-                       static_cast<uint8_t*>(a.out));
+                       gemm_xcd_chunk(a.max_rows, a.E), static_cast<uint8_t*>(a.out));
     return hipGetLastError();
 }
 

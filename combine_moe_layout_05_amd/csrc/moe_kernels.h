@@ -166,11 +166,23 @@ hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 // E experts, N output features, row tiles of row_tile rows and feature tiles
 // of `features`: every (feature tile, row tile) pair the worst routing can
 // need, rounded up to a multiple of 8 (one run of tiles per XCD).
+// How tiles are dealt to the 8 XCDs: 0 = one contiguous run of tile numbers
+// per XCD; c > 0 = chunks of c consecutive tiles dealt round-robin. Long
+// segments (at least 512 rows per expert at full capacity) use chunks of 16:
+// each XCD then gets a share of every expert instead of a few whole
+// experts, which evens out the HBM traffic the XCDs draw (measured on
+// MI355X at 32768 tokens, 256 experts: 14.5 vs 15.2 ms); shorter segments
+// keep the runs (3.59 vs 3.64 ms at 4096 tokens).
+inline int32_t gemm_xcd_chunk(int64_t max_rows, int32_t E) {
+    return max_rows >= int64_t(512) * E ? 16 : 0;
+}
 inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile,
                                  int32_t features) {
     const int64_t ftiles = (int64_t(N) + features - 1) / features;
     const int64_t tiles = ftiles * ((max_rows + row_tile - 1) / row_tile + E);
-    return (tiles + 7) / 8 * 8;
+    // Whole chunks per XCD, so the dealt tile numbers cover [0, grid).
+    const int64_t unit = 8 * int64_t(gemm_xcd_chunk(max_rows, E) > 0 ? gemm_xcd_chunk(max_rows, E) : 1);
+    return (tiles + unit - 1) / unit * unit;
 }
 constexpr int kGemmRowTileSmall = 64;
 constexpr int kGemmRowTileLarge = 128;
