@@ -299,3 +299,15 @@ def test_two_contexts_interleaved():
         assert_layout_equal(got, oracle.layout(ids, T, T, E, K), T)
     del c1, c2, outs
     _free()
+
+
+@pytest.mark.parametrize("E", [1, 3, 130])
+def test_expert_counts_off_the_quad_grid(E):
+    # E not a multiple of 4 (padded histogram rows) and E = 1 (one quad of
+    # experts, so the last workgroup's scan splits the tiles into 16 slices)
+    rng = np.random.default_rng(20 + E)
+    T, K = 3001, 8
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    ids[rng.random((T, K)) < 0.03] = -1
+    _check(_x(rng, T, 64, "bf16"), ids, rng.random((T, K)).astype(np.float32),
+           T, T, T, 64, E, K, "bf16")
