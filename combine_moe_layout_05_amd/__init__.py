@@ -1,4 +1,5 @@
-"""MI355X (gfx950) MoE token routing layout, dispatch and combine, their
+"""MI355X (gfx950) MoE token routing layout, dispatch and combine (layout and
+dispatch also fused into two launches: MoeDispatcher.layout_dispatch), their
 backward, and the expert step between them (a grouped GEMM driven by the
 device-side offsets).
 
