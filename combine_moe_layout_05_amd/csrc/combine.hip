@@ -142,16 +142,24 @@ void combine_kernel(const v4i* __restrict__ y_e, const int32_t* __restrict__ row
         if (all_valid) {
             // Every slot has an expert: the next chunk's loads are in flight
             // while this one is reduced and stored.
+            // Every chunk is loaded once: the loop runs while a chunk i + 2
+            // exists to prefetch, and the one or two chunks left run after it.
             v4i b0[K], b1[K];
             load(b0, 0);
             int32_t i = 0;
-            for (; i + 1 < iters; i += 2) {
+            for (; i + 2 < iters; i += 2) {
                 load(b1, i + 1);
                 emit(b0, i, true);
-                load(b0, min(i + 2, iters - 1));
+                load(b0, i + 2);
                 emit(b1, i + 1, true);
             }
-            if (i < iters) emit(b0, i, true);
+            if (i + 1 < iters) {
+                load(b1, i + 1);
+                emit(b0, i, true);
+                emit(b1, i + 1, true);
+            } else {
+                emit(b0, i, true);
+            }
             return;
         }
         for (int32_t i = 0; i < iters; ++i) {
