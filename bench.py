@@ -7,7 +7,9 @@ reads the dispatched buffer), moe_combine. The default workload is the
 DeepSeek-V3-shaped layer (T=4096, D=7168, E=256, top-8, bf16, Zipf(1.1)
 routing). Prints one JSON line. `value` and `ms_per_step` time K plain
 steps; the per-kernel times (and the roofline of the dominant kernel) come
-from a second pass of K steps with HIP events around each call.
+from a second pass of K steps with HIP events around each call (events
+created without the system-scope fence by default; a third pass with torch's
+default events is reported beside them).
 
 The line also carries, under "expert_step", the expert step between dispatch
 and combine (moe_grouped_gemm: one linear map per expert driven by the
@@ -46,6 +48,58 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class FenceFreeEvent:
+    """A HIP timing event created with hipEventDisableSystemFence.
+
+    A default event's record carries a system-scope release and acquire: the
+    command processor writes back and invalidates the caches at the marker,
+    and that work lands inside the interval being timed. HIP documents this
+    flag for events used only for timing. The event is recorded on torch's
+    current stream, the one every library call is launched on, through the
+    HIP runtime torch has already loaded.
+    """
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+
+            import torch
+            path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+            cls._hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._c = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                      ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+        stream = self._c.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = self._runtime().hipEventRecord(self.ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "FenceFreeEvent") -> float:
+        """Milliseconds from this event to `end` (both complete)."""
+        ms = self._c.c_float()
+        rc = self._runtime().hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -56,6 +110,9 @@ def parse_args():
                    help="iterations of the cache-flushed per-kernel measurement (0 = skip)")
     p.add_argument("--graph-replays", type=int, default=20,
                    help="timed replays of the step captured in a hipGraph (0 = skip)")
+    p.add_argument("--events", choices=["fence_free", "system"], default="fence_free",
+                   help="per-kernel timing events: created with hipEventDisableSystemFence "
+                        "(default) or torch's default events (system-scope fence at each record)")
     p.add_argument("--fused-steps", type=int, default=50,
                    help="also time the step with moe_layout_dispatch (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -295,16 +352,31 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    log(f"{K} steps with per-kernel events")
-    t_ev = time.perf_counter()
-    for i in range(K):
-        step(events[i])
-    torch.cuda.synchronize()
-    ms_per_step_events = (time.perf_counter() - t_ev) * 1e3 / K
-    lay_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dis_ms = [e[1].elapsed_time(e[2]) for e in events]
-    com_ms = [e[2].elapsed_time(e[3]) for e in events]
+    def timed_pass(make_event):
+        events = [[make_event() for _ in range(4)] for _ in range(K)]
+        t_ev = time.perf_counter()
+        for i in range(K):
+            step(events[i])
+        torch.cuda.synchronize()
+        per_step = (time.perf_counter() - t_ev) * 1e3 / K
+        return ([e[0].elapsed_time(e[1]) for e in events],
+                [e[1].elapsed_time(e[2]) for e in events],
+                [e[2].elapsed_time(e[3]) for e in events], per_step)
+
+    def torch_event():
+        return torch.cuda.Event(enable_timing=True)
+
+    main_event, other_event = ((FenceFreeEvent, torch_event) if args.events == "fence_free"
+                               else (torch_event, FenceFreeEvent))
+    log(f"{K} steps with per-kernel events ({args.events})")
+    lay_ms, dis_ms, com_ms, ms_per_step_events = timed_pass(main_event)
+    # The same pass with the other kind of event, reported for comparison.
+    o_lay, o_dis, o_com, o_step = timed_pass(other_event)
+    other_kind = "system" if args.events == "fence_free" else "fence_free"
+    other_events = {"events": other_kind, "step_us": round(o_step * 1e3, 2),
+                    "kernels_us": {"layout": round(float(np.mean(o_lay)) * 1e3, 2),
+                                   "dispatch": round(float(np.mean(o_dis)) * 1e3, 2),
+                                   "combine": round(float(np.mean(o_com)) * 1e3, 2)}}
     ms_per_step = elapsed * 1e3 / K
     value = w.T * K / elapsed
     avg = {"layout": float(np.mean(lay_ms)), "dispatch": float(np.mean(dis_ms)),
@@ -488,6 +560,8 @@ def main() -> int:
         "cold_cache": cold,
         "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
+        "kernel_events": args.events,
+        "kernels_with_other_events": other_events,
         "fused_layout_dispatch": fused,
         "backward": backward,
         "expert_step": expert,
