@@ -127,6 +127,8 @@ def parse_args():
     p.add_argument("--combine-block-waves", type=int, default=0)
     p.add_argument("--combine-store-nontemporal", type=int, default=-1,
                    help="1/0: streaming or ordinary stores of the combine output (-1: library default)")
+    p.add_argument("--layout-launches", type=int, default=0, choices=[-1, 0, 1, 2],
+                   help="1/2: force the one- or two-launch layout; -1 or 0: by size (default)")
     p.add_argument("--backward", type=int, default=0,
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--expert-iters", type=int, default=10,
@@ -317,7 +319,7 @@ def main() -> int:
                     bool(args.combine_nontemporal) if args.combine_nontemporal >= 0 else None,
                     args.dispatch_block_waves, args.combine_block_waves,
                     bool(args.combine_store_nontemporal) if args.combine_store_nontemporal >= 0
-                    else None)
+                    else None, args.layout_launches)
     tuning = disp.get_tuning()
     ntpr = w.ntpr
 

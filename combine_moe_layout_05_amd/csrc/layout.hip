@@ -13,7 +13,10 @@
 //                    or -1 (no expert, or padding t >= T)
 //   src_map[row]   = t*K+k
 //
-// Two launches, no atomics on global memory and no host round trip:
+// One launch up to kLayoutSingleMaxSlots slots (layout_single_kernel: each
+// workgroup counts the whole batch into LDS, then ranks its own tile), two
+// above it; either way no atomics on global memory and no host round trip.
+// The two-launch form:
 //   1. count: each workgroup histograms a tile of 512 or 1024 slots (chosen
 //      per call by the slot count) into LDS and writes
 //      its row of block_hist[tile][e].
@@ -238,6 +241,174 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
     }
 }
 
+// Single-launch layout. Workgroup b owns the tile of 1024*R slots starting at
+// b*1024*R. It first counts every slot of the batch into LDS, split into the
+// slots before its tile and the rest (one LDS integer add per slot; integer
+// adds commute, so the totals do not depend on their order). The exclusive
+// scan of the totals over experts gives the offsets (workgroup 0 writes
+// counts and offsets), and offsets plus the count before the tile give the
+// tile's first row per expert. The tile is then ranked as in
+// layout_rank_kernel: each wavefront ranks its run of R chunks in slot order
+// against a per-wavefront LDS running count, and per-expert prefixes over the
+// wavefronts give the final rows. Every workgroup reads the whole id array
+// (from L2 after the first), which bounds the batch size this form is used
+// for; no workgroup waits for another.
+template <int R>
+__global__ __launch_bounds__(kLayoutSingleThreads)
+void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t nslots,
+                          int32_t E, int bits, int32_t* __restrict__ counts,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ row_map,
+                          int32_t* __restrict__ src_map) {
+    constexpr int kWaves = kLayoutSingleThreads / 64;
+    constexpr int64_t kTile = int64_t(kLayoutSingleThreads) * R;
+    __shared__ int32_t wave_hist[kWaves][kMaxExperts];
+    __shared__ int32_t before[kMaxExperts];   // count before the tile, then the tile's first row
+    __shared__ int32_t rest[kMaxExperts];     // count from the tile on
+    __shared__ int32_t wave_sum[kWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t tile0 = int64_t(blockIdx.x) * kTile;
+
+    // The tile's own slots for the rank step, loaded first so that their
+    // latency overlaps the count: wavefront w holds slots
+    // tile0 + w*64*R + j*64 + lane.
+    const int64_t base = tile0 + wave * (64 * R);
+    int32_t ex[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
+
+    // Count copies: lane l adds into copy l % 8, split into the slots before
+    // the tile and the rest, so the lanes of one instruction that share an
+    // expert (a hot expert, or the same k-slot of neighbouring tokens) mostly
+    // hit different words. The copies live in wave_hist, which the rank step
+    // only needs afterwards.
+    constexpr int kCopies = 8;
+    static_assert(kCopies * 2 <= kWaves, "count copies fit in the per-wavefront histograms");
+    int32_t* cnt = &wave_hist[0][0];
+    int32_t* my_cnt = cnt + (lane % kCopies) * 2 * kMaxExperts;
+    for (int e = tid; e < E; e += kLayoutSingleThreads) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) wave_hist[w][e] = 0;
+    }
+    __syncthreads();
+
+    // Count every slot. The body is read as 16-byte quads of ids, thread tid
+    // taking quads tid, tid + 1024, ..., eight loads in flight before their
+    // adds; the slots before the first 16-byte boundary and after the last
+    // whole quad are read one by one. Ids outside [0, E) count nowhere.
+    {
+        auto add = [&](int32_t e, int64_t i) {
+            if (static_cast<uint32_t>(e) < static_cast<uint32_t>(E))
+                atomicAdd(&my_cnt[(i < tile0 ? 0 : kMaxExperts) + e], 1);
+        };
+        const int64_t mis = static_cast<int64_t>((reinterpret_cast<uintptr_t>(ids) >> 2) & 3);
+        const int64_t head = mis == 0 ? 0 : (4 - mis < nvalid ? 4 - mis : nvalid);
+        const int64_t nq = (nvalid - head) / 4;
+        const int64_t tail0 = head + 4 * nq;
+        if (tid < head) add(ids[tid], tid);
+        if (tail0 + tid < nvalid) add(ids[tail0 + tid], tail0 + tid);
+        const v4i* quads = reinterpret_cast<const v4i*>(ids + head);
+        constexpr int kU = 8;
+        constexpr int64_t kStep = kLayoutSingleThreads;
+        for (int64_t j0 = tid; j0 < nq; j0 += kU * kStep) {
+            v4i v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t j = j0 + u * kStep;
+                v[u] = j < nq ? quads[j] : v4i{-1, -1, -1, -1};
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t i = head + 4 * (j0 + u * kStep);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) add(v[u][c], i + c);
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kLayoutSingleThreads) {
+        int32_t b = 0, r = 0;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) {
+            b += cnt[(2 * c) * kMaxExperts + e];
+            r += cnt[(2 * c + 1) * kMaxExperts + e];
+        }
+        before[e] = b;
+        rest[e] = r;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kLayoutSingleThreads) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) wave_hist[w][e] = 0;
+    }
+    // (the barrier after the scan below orders these stores before the rank step)
+
+    // Exclusive scan of the totals over experts, one expert per thread
+    // (E <= kMaxExperts == kLayoutSingleThreads).
+    const int32_t mine_tot = tid < E ? before[tid] + rest[tid] : 0;
+    int32_t incl = mine_tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t up = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += up;
+    }
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - mine_tot;
+    for (int w = 0; w < wave; ++w) run += wave_sum[w];
+    if (tid < E) {
+        before[tid] += run;          // the tile's first row for expert tid
+        if (blockIdx.x == 0) {
+            counts[tid] = mine_tot;
+            offsets[tid] = run;
+        }
+    }
+    if (blockIdx.x == 0 && tid == kLayoutSingleThreads - 1) offsets[E] = run + mine_tot;
+
+    // Rank this tile's slots (loaded into ex[] above).
+    int32_t local[R];
+    int32_t* mine = wave_hist[wave];
+    const uint64_t below = lanes_below();
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const bool valid = ex[j] >= 0;
+        const uint64_t peers = peer_mask(ex[j], valid, bits);
+        const int32_t prior = valid ? mine[ex[j]] : 0;
+        local[j] = prior + __popcll(peers & below);
+        if (valid && (peers & below) == 0) mine[ex[j]] = prior + __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+
+    // Per-wavefront counts -> each wavefront's first row per expert.
+    for (int e = tid; e < E; e += kLayoutSingleThreads) {
+        int32_t r = before[e];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int32_t c = wave_hist[w][e];
+            wave_hist[w][e] = r;
+            r += c;
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t i = base + j * 64 + lane;
+        if (i >= nslots) continue;
+        if (ex[j] >= 0) {
+            const int32_t r = mine[ex[j]] + local[j];
+            row_map[i] = r;
+            // r < total <= nslots by construction; the bound only keeps a
+            // logic error from writing outside the buffer.
+            if (r >= 0 && r < nslots) src_map[r] = static_cast<int32_t>(i);
+        } else {
+            row_map[i] = -1;
+        }
+    }
+}
+
 // Completion counters of the fused count launch, one per context and device:
 // zero when the code object loads, and the last workgroup of every launch
 // puts its counter back to zero.
@@ -414,7 +585,28 @@ hipError_t launch_layout_count_scan(const LayoutArgs& a, int32_t counter_slot, i
                : launch_count_scan_r<kLayoutMaxSlotsPerLane>(a, counter_slot, stream);
 }
 
+template <int R>
+hipError_t launch_single_r(const LayoutArgs& a, hipStream_t stream) {
+    const int64_t tile = int64_t(kLayoutSingleThreads) * R;
+    const int64_t tiles = (a.nslots + tile - 1) / tile;
+    // At least one workgroup, so counts and offsets are written even for an
+    // empty capacity.
+    const uint32_t grid = static_cast<uint32_t>(tiles > 0 ? tiles : 1);
+    hipLaunchKernelGGL(layout_single_kernel<R>, dim3(grid), dim3(kLayoutSingleThreads), 0, stream,
+                       a.ids, a.nvalid, a.nslots, a.E, expert_bits(a.E), a.counts, a.offsets,
+                       a.row_map, a.src_map);
+    return hipGetLastError();
+}
+
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+    const bool single = a.launches == 1 || (a.launches == 0 && a.nslots <= kLayoutSingleMaxSlots);
+    if (single) {
+        switch (layout_single_slots_per_lane(a.nslots)) {
+            case 1: return launch_single_r<1>(a, stream);
+            case 2: return launch_single_r<2>(a, stream);
+            default: return launch_single_r<4>(a, stream);
+        }
+    }
     return layout_slots_per_lane(a.nslots) == kLayoutMinSlotsPerLane
                ? launch_r<kLayoutMinSlotsPerLane>(a, stream)
                : launch_r<kLayoutMaxSlotsPerLane>(a, stream);

@@ -247,6 +247,9 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     // last-level cache: it cannot stay cached for its consumer, and ordinary
     // stores would leave dirty lines to be written back during later kernels.
     c->tuning.combine_store_nontemporal = d.nmax4 * d.row_bytes > moe::kLastLevelCacheBytes ? 1 : 0;
+    // The layout runs as one launch up to kLayoutSingleMaxSlots slots, as
+    // two above (measured on MI355X).
+    c->tuning.layout_launches = -1;
     *out = c;
     return MOE_OK;
 }
@@ -268,8 +271,10 @@ int moe_set_tuning(moe_ctx* ctx, const moe_tuning* t) {
     if (t->dispatch_segments < 0 || t->dispatch_segments > moe::kMaxSegments ||
         t->combine_segments < 0 || t->combine_segments > moe::kMaxSegments ||
         t->dispatch_block_waves < 0 || t->dispatch_block_waves > moe::kMaxBlockWaves ||
-        t->combine_block_waves < 0 || t->combine_block_waves > moe::kMaxBlockWaves)
+        t->combine_block_waves < 0 || t->combine_block_waves > moe::kMaxBlockWaves ||
+        t->layout_launches < -1 || t->layout_launches > 2)
         return MOE_ERR_INVALID_ARG;
+    if (t->layout_launches) ctx->tuning.layout_launches = t->layout_launches;
     if (t->dispatch_segments) ctx->tuning.dispatch_segments = t->dispatch_segments;
     if (t->combine_segments) ctx->tuning.combine_segments = t->combine_segments;
     if (t->dispatch_block_waves) ctx->tuning.dispatch_block_waves = t->dispatch_block_waves;
@@ -300,6 +305,7 @@ static moe::LayoutArgs layout_args(const moe_ctx* ctx, const int32_t* d_ids, int
     a.offsets = at<int32_t>(ctx, ctx->desc.offsets);
     a.row_map = at<int32_t>(ctx, ctx->desc.row_map);
     a.src_map = at<int32_t>(ctx, ctx->desc.src_map);
+    a.launches = ctx->tuning.layout_launches > 0 ? ctx->tuning.layout_launches : 0;
     return a;
 }
 

@@ -385,15 +385,17 @@ class MoeDispatcher:
                    dispatch_nontemporal: Optional[bool] = None,
                    combine_nontemporal: Optional[bool] = None,
                    dispatch_block_waves: int = 0, combine_block_waves: int = 0,
-                   combine_store_nontemporal: Optional[bool] = None) -> None:
+                   combine_store_nontemporal: Optional[bool] = None,
+                   layout_launches: int = 0) -> None:
         """Launch shape only; results never depend on it. 0 / None keep the
-        current value."""
+        current value; layout_launches 1 or 2 forces one or two layout
+        launches, -1 chooses by size."""
         cur = self.get_tuning()
         dnt = cur["dispatch_nontemporal"] if dispatch_nontemporal is None else dispatch_nontemporal
         cnt = cur["combine_nontemporal"] if combine_nontemporal is None else combine_nontemporal
         snt = -1 if combine_store_nontemporal is None else int(combine_store_nontemporal)
         t = L.MoeTuning(dispatch_segments, combine_segments, int(dnt), int(cnt),
-                        dispatch_block_waves, combine_block_waves, snt)
+                        dispatch_block_waves, combine_block_waves, snt, layout_launches)
         L.check(self._lib.moe_set_tuning(self._ctx, C.byref(t)), "moe_set_tuning")
 
     def get_tuning(self) -> dict:
@@ -404,4 +406,5 @@ class MoeDispatcher:
                 "combine_nontemporal": bool(t.combine_nontemporal),
                 "dispatch_block_waves": t.dispatch_block_waves,
                 "combine_block_waves": t.combine_block_waves,
-                "combine_store_nontemporal": bool(t.combine_store_nontemporal)}
+                "combine_store_nontemporal": bool(t.combine_store_nontemporal),
+                "layout_launches": t.layout_launches}

@@ -358,7 +358,11 @@ int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t 
  * workgroup; 0 keeps the current value. A nonzero *_nontemporal marks
  * dispatch's expert-buffer stores / combine's expert-output loads / combine's
  * output stores as streaming (not kept in cache); for the last one -1 keeps
- * the current value. Results do not depend on any of these. Pure host. */
+ * the current value. layout_launches 1 runs moe_layout as one launch (every
+ * workgroup counts the whole batch, then ranks its tile), 2 as two (count,
+ * then offsets and rank), -1 chooses by size (one launch up to 32768
+ * slots, the default), 0 keeps the current value. Results do not depend on
+ * any of these. Pure host. */
 typedef struct moe_tuning {
     int32_t dispatch_segments;
     int32_t combine_segments;
@@ -367,6 +371,7 @@ typedef struct moe_tuning {
     int32_t dispatch_block_waves;
     int32_t combine_block_waves;
     int32_t combine_store_nontemporal;  /* streaming stores of y; -1 keeps */
+    int32_t layout_launches;            /* 1, 2, or -1 (by size); 0 keeps */
 } moe_tuning;
 int moe_set_tuning(moe_ctx *ctx, const moe_tuning *tuning);
 int moe_get_tuning(const moe_ctx *ctx, moe_tuning *out);

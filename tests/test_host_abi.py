@@ -295,7 +295,11 @@ def test_tuning_roundtrip_and_limits(lib):
     # 7168 bf16 = 896 chunks: 14 one-chunk segments; a dispatch workgroup per token row
     assert (t.dispatch_segments, t.dispatch_block_waves, t.combine_block_waves) == (14, 14, 16)
     assert t.combine_store_nontemporal == 0          # 58.7 MB output: stays cacheable
-    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1))) == L.MOE_OK
+    assert t.layout_launches == -1                   # layout launches chosen by size
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 2))) == L.MOE_OK
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.layout_launches == 2
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 1))) == L.MOE_OK
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.layout_launches == 1
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
     assert (t.dispatch_segments, t.combine_segments, t.dispatch_nontemporal, t.combine_nontemporal,
             t.dispatch_block_waves, t.combine_block_waves, t.combine_store_nontemporal) == \
@@ -305,11 +309,12 @@ def test_tuning_roundtrip_and_limits(lib):
     assert (t.dispatch_segments, t.combine_segments, t.dispatch_nontemporal, t.combine_nontemporal,
             t.dispatch_block_waves, t.combine_block_waves, t.combine_store_nontemporal) == \
         (4, 3, 0, 0, 2, 16, 1)
+    assert t.layout_launches == 1                    # 0 keeps the current value
     lib.moe_destroy(ctx)
     ctx, _, _ = _ctx(lib, _cfg(nmax=32768))         # 470 MB output: streamed
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_store_nontemporal == 1
     for bad in ((17, 1, 0, 0, 0, 0, 0), (-1, 1, 0, 0, 0, 0, 0), (1, 1, 0, 0, 17, 0, 0),
-                (1, 1, 0, 0, 0, -2, 0)):
+                (1, 1, 0, 0, 0, -2, 0), (1, 1, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, -2)):
         assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(*bad))) == L.MOE_ERR_INVALID_ARG
     lib.moe_destroy(ctx)
 
