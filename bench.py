@@ -115,6 +115,8 @@ def parse_args():
                         "(default) or torch's default events (system-scope fence at each record)")
     p.add_argument("--fused-steps", type=int, default=50,
                    help="also time the step with moe_layout_dispatch (0 = skip)")
+    p.add_argument("--cpu-single-seconds", type=float, default=3.0,
+                   help="budget of the single-threaded oracle sample (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget of the oracle CPU baseline (0 = skip)")
     p.add_argument("--dispatch-segments", type=int, default=0)
@@ -514,23 +516,31 @@ def main() -> int:
                 "algorithmic_bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg[dominant] * 1e3, 2)}
 
-    cpu = None
-    if args.cpu_seconds > 0:
+    def oracle_rate(threads: int, budget_s: float) -> dict:
         import oracle
-        cores = max(1, min(16, len(os.sched_getaffinity(0))))
-        log(f"oracle CPU baseline on {cores} threads, ~{args.cpu_seconds:.0f} s")
+        log(f"oracle CPU baseline on {threads} thread(s), ~{budget_s:.0f} s")
         n, t_start = 0, time.perf_counter()
         while True:
             oracle.run_pipeline(b["x"], b["ids"], b["scores"], w.T, ntpr, w.E, w.K,
-                                nthreads=cores)
+                                nthreads=threads)
             n += 1
-            if time.perf_counter() - t_start >= args.cpu_seconds:
+            if time.perf_counter() - t_start >= budget_s:
                 break
         cpu_s = time.perf_counter() - t_start
-        cpu = {"value": round(w.T * n / cpu_s, 1), "unit": "tokens/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"{n} full {w.name} batches (T={w.T}) through the oracle's "
-                         f"layout+dispatch+combine, {cpu_s:.1f} s"}
+        return {"value": round(w.T * n / cpu_s, 1), "unit": "tokens/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"{n} full {w.name} batches (T={w.T}) through the oracle's "
+                          f"layout+dispatch+combine, {cpu_s:.1f} s"}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = oracle_rate(max(1, min(16, len(os.sched_getaffinity(0)))), args.cpu_seconds)
+    cpu_single = oracle_rate(1, args.cpu_single_seconds) if args.cpu_single_seconds > 0 else None
+
+    def interval_stats(ms) -> dict:
+        us = np.asarray(ms, dtype=np.float64) * 1e3
+        return {"mean": round(float(us.mean()), 2), "median": round(float(np.median(us)), 2),
+                "min": round(float(us.min()), 2), "p90": round(float(np.percentile(us, 90)), 2)}
 
     out = {
         "metric": METRIC,
@@ -551,8 +561,11 @@ def main() -> int:
                    "scores": w.scores, "parallelism": "single-gpu", "tuning": tuning},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_single_thread": cpu_single,
         "kernels_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "kernels_gbps": {k: round(v, 1) for k, v in gbps.items()},
+        "kernels_us_stats": {"layout": interval_stats(lay_ms), "dispatch": interval_stats(dis_ms),
+                             "combine": interval_stats(com_ms)},
         "dispatch_combine": {
             "us": round(dc_ms * 1e3, 2),
             "tokens_per_s": round(w.T / (dc_ms * 1e-3), 1),
