@@ -131,6 +131,8 @@ def parse_args():
                    help="1/0: streaming or ordinary stores of the combine output (-1: library default)")
     p.add_argument("--layout-launches", type=int, default=0, choices=[-1, 0, 1, 2],
                    help="1/2: force the one- or two-launch layout; -1 or 0: by size (default)")
+    p.add_argument("--dispatch-store-burst", type=int, default=0, choices=[0, 1, 2],
+                   help="1/2: back-to-back or paced dispatch stores; 0: library default (paced)")
     p.add_argument("--backward", type=int, default=0,
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--expert-iters", type=int, default=10,
@@ -321,7 +323,7 @@ def main() -> int:
                     bool(args.combine_nontemporal) if args.combine_nontemporal >= 0 else None,
                     args.dispatch_block_waves, args.combine_block_waves,
                     bool(args.combine_store_nontemporal) if args.combine_store_nontemporal >= 0
-                    else None, args.layout_launches)
+                    else None, args.layout_launches, args.dispatch_store_burst)
     tuning = disp.get_tuning()
     ntpr = w.ntpr
 

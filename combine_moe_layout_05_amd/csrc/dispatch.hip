@@ -51,14 +51,16 @@ __device__ __forceinline__ v4i transform(float s, v4i v) {
 }
 
 // The copy of one wavefront's item: its K rows from the staged row map, the
-// row chunk(s) stored K times, and (first segment) the slots' scores.
-template <int K, bool NT, bool SINGLE, int MODE>
+// row chunk(s) stored K times, and (first segment) the slots' scores. BURST
+// (single-chunk shape only): the K stores issue back to back.
+template <int K, bool NT, bool SINGLE, int MODE, bool BURST>
 __device__ __forceinline__ void copy_rows(const float* __restrict__ scores,
                                           int32_t chunks, v4i* __restrict__ x_e,
                                           float* __restrict__ s_e, const int32_t* tile_rows,
                                           const float* tile_scores, int64_t t, int64_t t_first,
                                           int seg, int32_t c_begin, int32_t c_end,
-                                          const v4i* src, v4i early, int lane) {
+                                          const v4i* src, v4i early, float early_score,
+                                          int lane) {
     constexpr int U = kDispatchUnroll;
     const int32_t* rows = tile_rows + (t - t_first) * K;
     int32_t row[K];
@@ -73,23 +75,30 @@ __device__ __forceinline__ void copy_rows(const float* __restrict__ scores,
     }
 
     // Lane k < K of the first segment also moves slot k's score (after the
-    // row stores, which it would otherwise hold up).
+    // row stores, which it would otherwise hold up). In the single-chunk
+    // shape the score was loaded with the row chunk, at kernel entry.
     auto move_score = [&]() {
         if (seg == 0 && lane < K) {
             const int32_t r = rows[lane];
-            if (r >= 0) s_e[r] = scores[t * K + lane];
+            if (r >= 0) s_e[r] = SINGLE ? early_score : scores[t * K + lane];
         }
     };
 
     // Each slot's store sits behind its own "has an expert" branch, and the
-    // compiler waits for all outstanding memory operations before each one,
-    // so a wavefront's K stores go out one after another. Marking the loaded
-    // chunk ready once (so the K stores issue back to back) measured slower
-    // on MI355X: dispatch 82.7 vs 80.7 us at the DSV3 shape, 805 vs 788 us at
-    // the 32k-token shape; the paced stores are kept.
+    // compiler waits for all outstanding memory operations before each one
+    // (stores count in the same counter as loads), so a wavefront's K stores
+    // go out one after another. BURST waits for the loaded chunk once: the
+    // empty asm statement below redefines the chunk's registers after an
+    // explicit wait, so the compiler sees them ready and issues the K stores
+    // back to back. Measured on MI355X, pacing is the faster default: dispatch
+    // 79.0 vs 80.8 us at the DSV3 shape, 788 vs 809 us at the 32k-token
+    // shape, 21.7 vs 20.4-21.4 us at 2048 tokens of 4 KiB with the step no
+    // faster; back to back wins only at 8192 tokens of 8 KiB (95.0 vs
+    // 96.7 us).
     if constexpr (SINGLE) {
         const int32_t c = c_begin + lane;
         if (c < c_end) {
+            if constexpr (BURST) asm volatile("s_waitcnt vmcnt(0)" : "+v"(early));
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 if (row[k] >= 0)
@@ -143,7 +152,7 @@ struct RankArgs {
 // copied in groups of U chunks per lane, then one chunk at a time. RANK: the
 // workgroup computes its tokens' rows (and writes them to row_map and
 // src_map) instead of reading row_map.
-template <int K, bool NT, bool SINGLE, int MODE, bool RANK>
+template <int K, bool NT, bool SINGLE, int MODE, bool RANK, bool BURST>
 __global__ __launch_bounds__(kMaxBlockThreads)
 void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores,
                      const int32_t* __restrict__ row_map, int32_t T, int32_t chunks,
@@ -175,9 +184,11 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     const int32_t c_end = min(c_begin + seg_chunks, chunks);
     const v4i* src = x + t * chunks;
     v4i early = {0, 0, 0, 0};
+    float early_score = 0.0f;
     if constexpr (SINGLE) {
         const int32_t c = c_begin + lane;
         if (live && c < c_end) early = src[c];
+        if (live && seg == 0 && lane < K) early_score = scores[t * K + lane];
     }
     // RANK: the row this thread records in row_map / src_map after the copy
     // (stores issued here would hold up the copy's first wait).
@@ -242,8 +253,9 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     __syncthreads();
 
     if (live)
-        copy_rows<K, NT, SINGLE, MODE>(scores, chunks, x_e, s_e, tile_rows, tile_scores, t, t_first,
-                                       seg, c_begin, c_end, src, early, lane);
+        copy_rows<K, NT, SINGLE, MODE, BURST>(scores, chunks, x_e, s_e, tile_rows, tile_scores, t,
+                                              t_first, seg, c_begin, c_end, src, early,
+                                              early_score, lane);
     if constexpr (RANK) {
         if (rec_slot >= 0) {
             rk.row_map[rec_slot] = rec_row;
@@ -253,29 +265,39 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
 }
 
 
-template <int K, bool RANK>
-hipError_t launch_k(const DispatchArgs& a, const RankArgs& rk, int32_t segments,
-                    int32_t seg_chunks, hipStream_t stream) {
+template <int K, bool RANK, bool BURST>
+hipError_t launch_kb(const DispatchArgs& a, const RankArgs& rk, int32_t segments,
+                     int32_t seg_chunks, hipStream_t stream) {
     const int64_t items = int64_t(a.T) * segments;
     const int64_t blocks = (items + a.block_waves - 1) / a.block_waves;
     const bool single = seg_chunks == 64;
-    decltype(&dispatch_kernel<K, false, true, kCopy, RANK>) kernel;
+    decltype(&dispatch_kernel<K, false, true, kCopy, RANK, BURST>) kernel;
+    // BURST only changes the single-chunk copy; the multi-chunk copy has one
+    // instantiation (BURST = false).
     if (a.scaled) {  // streaming stores are not offered with the scores applied
-        kernel = a.bf16 ? (single ? dispatch_kernel<K, false, true, kScaleBF16, RANK>
-                                  : dispatch_kernel<K, false, false, kScaleBF16, RANK>)
-                        : (single ? dispatch_kernel<K, false, true, kScaleF32, RANK>
-                                  : dispatch_kernel<K, false, false, kScaleF32, RANK>);
+        kernel = a.bf16 ? (single ? dispatch_kernel<K, false, true, kScaleBF16, RANK, BURST>
+                                  : dispatch_kernel<K, false, false, kScaleBF16, RANK, false>)
+                        : (single ? dispatch_kernel<K, false, true, kScaleF32, RANK, BURST>
+                                  : dispatch_kernel<K, false, false, kScaleF32, RANK, false>);
     } else {
-        kernel = a.nontemporal ? (single ? dispatch_kernel<K, true, true, kCopy, RANK>
-                                         : dispatch_kernel<K, true, false, kCopy, RANK>)
-                               : (single ? dispatch_kernel<K, false, true, kCopy, RANK>
-                                         : dispatch_kernel<K, false, false, kCopy, RANK>);
+        kernel = a.nontemporal ? (single ? dispatch_kernel<K, true, true, kCopy, RANK, BURST>
+                                         : dispatch_kernel<K, true, false, kCopy, RANK, false>)
+                               : (single ? dispatch_kernel<K, false, true, kCopy, RANK, BURST>
+                                         : dispatch_kernel<K, false, false, kCopy, RANK, false>);
     }
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * a.block_waves), 0,
                        stream, static_cast<const v4i*>(a.x), a.scores, a.row_map, a.T,
                        a.chunks, segments, seg_chunks, a.max_rows, static_cast<v4i*>(a.x_e),
                        a.s_e, rk);
     return hipGetLastError();
+}
+
+template <int K, bool RANK>
+hipError_t launch_k(const DispatchArgs& a, const RankArgs& rk, int32_t segments,
+                    int32_t seg_chunks, hipStream_t stream) {
+    const bool burst = seg_chunks == 64 && a.store_burst;
+    return burst ? launch_kb<K, RANK, true>(a, rk, segments, seg_chunks, stream)
+                 : launch_kb<K, RANK, false>(a, rk, segments, seg_chunks, stream);
 }
 
 template <bool RANK>

@@ -250,6 +250,9 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     // The layout runs as one launch up to kLayoutSingleMaxSlots slots, as
     // two above (measured on MI355X).
     c->tuning.layout_launches = -1;
+    // Dispatch stores are paced: each waits for the previous one (measured
+    // on MI355X the faster default; back to back is a tuning option).
+    c->tuning.dispatch_store_burst = 2;
     *out = c;
     return MOE_OK;
 }
@@ -272,9 +275,11 @@ int moe_set_tuning(moe_ctx* ctx, const moe_tuning* t) {
         t->combine_segments < 0 || t->combine_segments > moe::kMaxSegments ||
         t->dispatch_block_waves < 0 || t->dispatch_block_waves > moe::kMaxBlockWaves ||
         t->combine_block_waves < 0 || t->combine_block_waves > moe::kMaxBlockWaves ||
-        t->layout_launches < -1 || t->layout_launches > 2)
+        t->layout_launches < -1 || t->layout_launches > 2 ||
+        t->dispatch_store_burst < 0 || t->dispatch_store_burst > 2)
         return MOE_ERR_INVALID_ARG;
     if (t->layout_launches) ctx->tuning.layout_launches = t->layout_launches;
+    if (t->dispatch_store_burst) ctx->tuning.dispatch_store_burst = t->dispatch_store_burst;
     if (t->dispatch_segments) ctx->tuning.dispatch_segments = t->dispatch_segments;
     if (t->combine_segments) ctx->tuning.combine_segments = t->combine_segments;
     if (t->dispatch_block_waves) ctx->tuning.dispatch_block_waves = t->dispatch_block_waves;
@@ -324,6 +329,7 @@ static moe::DispatchArgs dispatch_args(const moe_ctx* ctx, const void* d_x, cons
     a.segments = ctx->tuning.dispatch_segments;
     a.block_waves = ctx->tuning.dispatch_block_waves;
     a.nontemporal = ctx->tuning.dispatch_nontemporal != 0;
+    a.store_burst = ctx->tuning.dispatch_store_burst == 1;
     a.scaled = scaled;
     a.bf16 = ctx->cfg.dtype == MOE_BF16;
     return a;

@@ -361,7 +361,10 @@ int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t 
  * the current value. layout_launches 1 runs moe_layout as one launch (every
  * workgroup counts the whole batch, then ranks its tile), 2 as two (count,
  * then offsets and rank), -1 chooses by size (one launch up to 32768
- * slots, the default), 0 keeps the current value. Results do not depend on
+ * slots, the default), 0 keeps the current value. dispatch_store_burst 1
+ * issues each wavefront's K row stores back to back, 2 issues each after the
+ * previous one has completed (the default), 0 keeps the current value; it
+ * applies to the default one-chunk-per-lane shape. Results do not depend on
  * any of these. Pure host. */
 typedef struct moe_tuning {
     int32_t dispatch_segments;
@@ -372,6 +375,7 @@ typedef struct moe_tuning {
     int32_t combine_block_waves;
     int32_t combine_store_nontemporal;  /* streaming stores of y; -1 keeps */
     int32_t layout_launches;            /* 1, 2, or -1 (by size); 0 keeps */
+    int32_t dispatch_store_burst;       /* 1 back to back, 2 paced; 0 keeps */
 } moe_tuning;
 int moe_set_tuning(moe_ctx *ctx, const moe_tuning *tuning);
 int moe_get_tuning(const moe_ctx *ctx, moe_tuning *out);

@@ -33,9 +33,11 @@ def _double_bf16(x_bits: np.ndarray) -> np.ndarray:
 class Captured:
     """Static inputs, the dispatcher and one captured graph."""
 
-    def __init__(self):
+    def __init__(self, tuning=None):
         N, D, K = W.nmax, W.D, W.K
         self.disp = MoeDispatcher(N, D, W.E, K, dtype=torch.bfloat16, device=DEV)
+        if tuning:
+            self.disp.set_tuning(**tuning)
         self.x = torch.zeros((N, D), dtype=torch.bfloat16, device=DEV)
         self.ids = torch.full((N, K), -1, dtype=torch.int32, device=DEV)
         self.s = torch.zeros((N, K), dtype=torch.float32, device=DEV)
@@ -132,6 +134,40 @@ def test_graph_replays_with_fresh_routing(cap, chunk):
             np.testing.assert_array_equal(ce, o2["counts"])
             np.testing.assert_array_equal(oe, o2["offsets"])
             assert np.array_equal(ye, o2["y"])
+
+
+@pytest.fixture(scope="module")
+def cap_other_forms():
+    # The one-launch layout (forced at 65536 slots: 2048-slot tiles) and
+    # back-to-back dispatch stores, the forms the defaults do not take here.
+    note("graph: capture at 8192 tokens, one-launch layout, back-to-back stores")
+    c = Captured(tuning={"layout_launches": 1, "dispatch_store_burst": 1})
+    yield c
+    del c
+    torch.cuda.empty_cache()
+
+
+def test_graph_replays_other_launch_forms(cap_other_forms):
+    c = cap_other_forms
+    for i in list(range(0, 12)) + [17, 27, 37, 45, 59]:
+        b = workloads.replay_batch(i)
+        T = b["T"]
+        note(f"graph replay (other forms) {i} T={T}")
+        c.load(b)
+        if i % 10 == 7:
+            c.disp.workspace.fill_(0xFF)
+            c.y_e.fill_(0xFF)
+        c.graph.replay()
+        sync_or_fail()
+        y = x_to_np(c.y)
+        o = _oracle(b, T, T)
+        np.testing.assert_array_equal(c.disp.counts.cpu().numpy(), o["counts"])
+        np.testing.assert_array_equal(c.disp.offsets.cpu().numpy(), o["offsets"])
+        assert np.array_equal(y[:T], o["y"])
+        assert (y[T:] == 0).all()
+        if i % 10 == 5:
+            ye, ce, _ = c.eager(b["x"], b["ids"], b["scores"], T, T)
+            assert np.array_equal(ye, y[:T])
 
 
 def test_graph_buckets_with_different_capacities_share_one_context():

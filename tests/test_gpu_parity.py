@@ -219,7 +219,7 @@ def test_poisoned_workspace(name, T):
 # ---------------------------------------------------------------------------
 # Edge cases
 
-def _edge(T, ntpr, nmax, D, E, K, dtype, ids, scores=None, seed=0, segments=None):
+def _edge(T, ntpr, nmax, D, E, K, dtype, ids, scores=None, seed=0, segments=None, tuning=None):
     rng = np.random.default_rng(seed)
     xf = rng.standard_normal((max(T, 1), D)).astype(np.float32)
     if dtype == "bf16":
@@ -235,7 +235,10 @@ def _edge(T, ntpr, nmax, D, E, K, dtype, ids, scores=None, seed=0, segments=None
                         combine_nontemporal=bool(segments[2]),
                         dispatch_block_waves=segments[3], combine_block_waves=segments[4],
                         combine_store_nontemporal=bool(segments[2]))
-    note(f"edge T={T} ntpr={ntpr} nmax={nmax} D={D} E={E} K={K} {dtype} seg={segments}")
+    if tuning:
+        disp.set_tuning(**tuning)
+    note(f"edge T={T} ntpr={ntpr} nmax={nmax} D={D} E={E} K={K} {dtype} seg={segments} "
+         f"tuning={tuning}")
     g = run_gpu(disp, x, ids, scores, T, ntpr)
     o = oracle.run_pipeline(x, ids, scores, T, ntpr, E, K)
     assert_layout_equal(g, o, T)
@@ -297,6 +300,34 @@ def test_ragged_row_and_launch_shapes(segments):
     _edge(T, 1003, 2048, 200, E, K, "bf16", ids, segments=segments)   # 25 chunks per row
     _edge(T, T, T, 7168, E, K, "bf16", ids, segments=segments)        # 896 chunks per row
     _edge(T, T, T, 36, E, K, "f32", ids, segments=segments)           # 9 chunks per row
+
+
+@pytest.mark.parametrize("burst", [1, 2])
+@pytest.mark.parametrize("name,T", [("tiny", 61), ("padded", 614), ("padded", 2047),
+                                    ("dsv3", 4096)])
+def test_dispatch_store_schedules(name, T, burst):
+    """Both store schedules of the one-chunk dispatch (a wavefront's K row
+    stores back to back, or each after the previous one) give the oracle's
+    buffers bit for bit."""
+    w = workloads.WORKLOADS[name]
+    b = workloads.make_batch(w)
+    disp = _dispatcher(w)
+    disp.set_tuning(dispatch_store_burst=burst)
+    assert disp.get_tuning()["dispatch_store_burst"] == burst
+    _full_check(disp, b, T, w.ntpr, w.E, w.K)
+    del disp
+    _free()
+
+
+@pytest.mark.parametrize("burst", [1, 2])
+def test_dispatch_store_schedules_with_no_expert_slots(burst):
+    rng = np.random.default_rng(8)
+    T, E, K = 777, 64, 8
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    ids[rng.random((T, K)) < 0.2] = -1
+    ids[::5] = -1                                                     # whole tokens with no expert
+    _edge(T, 779, 1024, 2048, E, K, "bf16", ids, tuning={"dispatch_store_burst": burst})
+    _edge(T, T, T, 7168, E, K, "bf16", ids, tuning={"dispatch_store_burst": burst})
 
 
 def test_unaligned_capacity_rounds_up():

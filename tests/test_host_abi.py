@@ -296,10 +296,14 @@ def test_tuning_roundtrip_and_limits(lib):
     assert (t.dispatch_segments, t.dispatch_block_waves, t.combine_block_waves) == (14, 14, 16)
     assert t.combine_store_nontemporal == 0          # 58.7 MB output: stays cacheable
     assert t.layout_launches == -1                   # layout launches chosen by size
+    assert t.dispatch_store_burst == 2               # dispatch stores paced by default
     assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 2))) == L.MOE_OK
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.layout_launches == 2
     assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 1))) == L.MOE_OK
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.layout_launches == 1
+    assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 0, 2))) == L.MOE_OK
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
+    assert (t.layout_launches, t.dispatch_store_burst) == (1, 2)
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
     assert (t.dispatch_segments, t.combine_segments, t.dispatch_nontemporal, t.combine_nontemporal,
             t.dispatch_block_waves, t.combine_block_waves, t.combine_store_nontemporal) == \
@@ -314,7 +318,8 @@ def test_tuning_roundtrip_and_limits(lib):
     ctx, _, _ = _ctx(lib, _cfg(nmax=32768))         # 470 MB output: streamed
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_store_nontemporal == 1
     for bad in ((17, 1, 0, 0, 0, 0, 0), (-1, 1, 0, 0, 0, 0, 0), (1, 1, 0, 0, 17, 0, 0),
-                (1, 1, 0, 0, 0, -2, 0), (1, 1, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, -2)):
+                (1, 1, 0, 0, 0, -2, 0), (1, 1, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, -2),
+                (1, 1, 0, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, 0, -1)):
         assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(*bad))) == L.MOE_ERR_INVALID_ARG
     lib.moe_destroy(ctx)
 
