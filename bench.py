@@ -460,12 +460,12 @@ def main() -> int:
         for i in range(args.cold_iters):
             lay = disp.layout(ids, ntpr)
             torch.sum(scratch, dim=0, out=sink)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = main_event(), main_event()
             e0.record()
             disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
             e1.record()
             torch.sum(scratch, dim=0, out=sink)
-            e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e2, e3 = main_event(), main_event()
             e2.record()
             disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
             e3.record()
@@ -486,7 +486,7 @@ def main() -> int:
                          device=dev).to(dt)
         lay = disp.layout(ids, ntpr)
         disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
-        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        bev = [[main_event() for _ in range(3)]
                for _ in range(args.backward + 2)]
         for e in bev:
             e[0].record()
