@@ -96,6 +96,25 @@ static void one_config(int32_t nmax, int32_t D, int32_t E, int32_t K, int32_t dt
     EXPECT(moe_set_tuning(ctx, &t) == MOE_OK);
     t.dispatch_segments = 99;
     EXPECT(moe_set_tuning(ctx, &t) != MOE_OK);
+    // both layout forms and both dispatch store forms, forced, then bad values
+    for (int32_t lf : {1, 2, -1}) {
+        for (int32_t sb : {1, 2}) {
+            EXPECT(moe_get_tuning(ctx, &t) == MOE_OK);
+            t.layout_launches = lf;
+            t.dispatch_store_burst = sb;
+            EXPECT(moe_set_tuning(ctx, &t) == MOE_OK);
+            EXPECT(moe_layout(ctx, static_cast<const int32_t*>(p), ntpr, ntpr, nullptr) == MOE_OK);
+            EXPECT(moe_dispatch(ctx, p, static_cast<const float*>(p),
+                                static_cast<const int32_t*>(p), counts, ntpr, ntpr,
+                                nullptr) == MOE_OK);
+        }
+    }
+    EXPECT(moe_get_tuning(ctx, &t) == MOE_OK);
+    t.layout_launches = 3;
+    EXPECT(moe_set_tuning(ctx, &t) == MOE_ERR_INVALID_ARG);
+    t.layout_launches = 0;
+    t.dispatch_store_burst = -1;
+    EXPECT(moe_set_tuning(ctx, &t) == MOE_ERR_INVALID_ARG);
     EXPECT(moe_destroy(ctx) == MOE_OK);
 }
 

@@ -21,6 +21,7 @@ static void require(bool ok, const char* what) {
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t) {
     require(a.E >= 1 && a.nvalid >= 0 && a.nslots >= a.nvalid, "layout sizes");
+    require(a.launches >= 0 && a.launches <= 2, "layout launches");
     ++g_launches;
     return hipSuccess;
 }
