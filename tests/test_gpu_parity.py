@@ -100,6 +100,35 @@ def test_prefill32k_parity(name):
     _free()
 
 
+def test_expert_buffer_past_4_gib():
+    """40960 tokens of 14 KiB rows (327680 dispatched rows, 4.70 GB of x_e):
+    rows past byte offset 2^32 are written by dispatch and read by combine
+    (64-bit addressing), and the layout runs its two-launch form at 327680
+    slots. Layout, s_e, every x_e row (in slices) and y against the oracle."""
+    w = workloads.Workload("past_4_gib", T=40960, ntpr=40960, nmax=40960, D=7168, E=256, K=8,
+                           dtype="bf16", routing="zipf", zipf_s=1.2, scores="sigmoid_norm",
+                           seed=3)
+    note("past 4 GiB: drawing inputs")
+    b = workloads.make_batch(w)
+    disp = _dispatcher(w)
+    assert disp.desc.max_rows * w.D * 2 > 1 << 32
+    note("past 4 GiB: GPU pipeline")
+    g = run_gpu(disp, b["x"], b["ids"], b["scores"], w.T, w.ntpr, copy_x_e=False)
+    note("past 4 GiB: oracle")
+    o = oracle.run_pipeline(b["x"], b["ids"], b["scores"], w.T, w.ntpr, w.E, w.K,
+                            nthreads=ORACLE_THREADS)
+    assert o["total"] == w.T * w.K and o["total"] * w.D * 2 > 1 << 32
+    assert_layout_equal(g, o, w.T)
+    assert np.array_equal(g["s_e"].view(np.uint32), o["s_e"].view(np.uint32))
+    step = 1 << 15
+    for r0 in range(0, o["total"], step):
+        r1 = min(r0 + step, o["total"])
+        assert np.array_equal(x_to_np(disp.x_e[r0:r1]), o["x_e"][r0:r1]), (r0, r1)
+    assert np.array_equal(g["y"], o["y"])
+    del disp, o
+    _free()
+
+
 def test_graph_shape_full_capacity_parity():
     w = workloads.WORKLOADS["graph"]
     b = workloads.make_batch(w, T=w.nmax, seed=w.seed + 1)
