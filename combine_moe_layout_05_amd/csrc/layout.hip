@@ -261,7 +261,9 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
                           int32_t* __restrict__ src_map) {
     constexpr int kWaves = kLayoutSingleThreads / 64;
     constexpr int64_t kTile = int64_t(kLayoutSingleThreads) * R;
-    __shared__ int32_t wave_hist[kWaves][kMaxExperts];
+    // Per-wavefront rank counts, wavefront w at [w * kMaxExperts, ...); the
+    // count step uses the same words for its copies first.
+    __shared__ int32_t wave_hist[kWaves * kMaxExperts];
     __shared__ int32_t before[kMaxExperts];   // count before the tile, then the tile's first row
     __shared__ int32_t rest[kMaxExperts];     // count from the tile on
     __shared__ int32_t wave_sum[kWaves];
@@ -285,11 +287,11 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
     // only needs afterwards.
     constexpr int kCopies = 8;
     static_assert(kCopies * 2 <= kWaves, "count copies fit in the per-wavefront histograms");
-    int32_t* cnt = &wave_hist[0][0];
+    int32_t* cnt = wave_hist;
     int32_t* my_cnt = cnt + (lane % kCopies) * 2 * kMaxExperts;
     for (int e = tid; e < E; e += kLayoutSingleThreads) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) wave_hist[w][e] = 0;
+        for (int w = 0; w < kWaves; ++w) wave_hist[w * kMaxExperts + e] = 0;
     }
     __syncthreads();
 
@@ -340,7 +342,7 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
     __syncthreads();
     for (int e = tid; e < E; e += kLayoutSingleThreads) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) wave_hist[w][e] = 0;
+        for (int w = 0; w < kWaves; ++w) wave_hist[w * kMaxExperts + e] = 0;
     }
     // (the barrier after the scan below orders these stores before the rank step)
 
@@ -368,7 +370,7 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
 
     // Rank this tile's slots (loaded into ex[] above).
     int32_t local[R];
-    int32_t* mine = wave_hist[wave];
+    int32_t* mine = wave_hist + wave * kMaxExperts;
     const uint64_t below = lanes_below();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -386,8 +388,8 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
         int32_t r = before[e];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const int32_t c = wave_hist[w][e];
-            wave_hist[w][e] = r;
+            const int32_t c = wave_hist[w * kMaxExperts + e];
+            wave_hist[w * kMaxExperts + e] = r;
             r += c;
         }
     }
