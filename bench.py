@@ -115,6 +115,8 @@ def parse_args():
                         "(default) or torch's default events (system-scope fence at each record)")
     p.add_argument("--fused-steps", type=int, default=50,
                    help="also time the step with moe_layout_dispatch (0 = skip)")
+    p.add_argument("--copy-reference", type=int, default=1,
+                   help="1: also time a plain 1 GiB device write and copy (0 = skip)")
     p.add_argument("--cpu-single-seconds", type=float, default=3.0,
                    help="budget of the single-threaded oracle sample (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -181,6 +183,32 @@ def counter_traffic(kind: str, workload: str):
     if rec.get("kernel_source_sha256") != source_digest(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def device_copy_rates(mib: int = 1024, reps: int = 10) -> dict:
+    """Rates of a plain device write (torch fill_) and copy (HIP copyBuffer
+    through torch copy_) of `mib` MiB, timed like the path's kernels: a
+    reference for what a plain streaming kernel reaches on this GPU."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    res = {"bytes": n}
+    for name, fn, nbytes in (("write", lambda: a.fill_(3), n), ("copy", lambda: b.copy_(a), 2 * n)):
+        e0, e1 = FenceFreeEvent(), FenceFreeEvent()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[f"{name}_gbps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return res
 
 
 def calibrate_copy(mib: int) -> None:
@@ -529,10 +557,21 @@ def main() -> int:
             if time.perf_counter() - t_start >= budget_s:
                 break
         cpu_s = time.perf_counter() - t_start
-        return {"value": round(w.T * n / cpu_s, 1), "unit": "tokens/s", "cores": threads,
+        rate = w.T * n / cpu_s
+        return {"value": round(rate, 1), "unit": "tokens/s", "cores": threads,
                 "kind": "oracle",
+                "gbps": round(rate * (bytes_per_token(w, "dispatch") +
+                                      bytes_per_token(w, "combine")) / 1e9, 2),
                 "sample": f"{n} full {w.name} batches (T={w.T}) through the oracle's "
-                          f"layout+dispatch+combine, {cpu_s:.1f} s"}
+                          f"layout+dispatch+combine, {cpu_s:.1f} s; gbps counts the "
+                          f"dispatch+combine algorithmic bytes"}
+
+    ref = None
+    if args.copy_reference:
+        log("device write/copy reference, 1 GiB")
+        ref = device_copy_rates()
+        ref["dispatch_combine_over_copy"] = round(
+            dc_bytes / (dc_ms * 1e-3) / 1e9 / ref["copy_gbps"], 4)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -575,6 +614,7 @@ def main() -> int:
             "frac_of_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "cold_cache": cold,
+        "device_copy_reference": ref,
         "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "kernel_events": args.events,
