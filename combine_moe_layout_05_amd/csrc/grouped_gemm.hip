@@ -13,9 +13,10 @@
 // expert's segment), F = 32 per wavefront. Within an expert, tiles go in
 // blocks of up to 8 row tiles: all feature tiles of a block, each with the
 // block's row tiles fastest. Workgroups are dealt to the 8 XCDs round-robin,
-// so each XCD is given a contiguous run of tile numbers (or, for long
-// segments, every eighth chunk of 16 tile numbers); the workgroups an XCD
-// runs at once then cover a few row tiles x feature tiles of one expert,
+// so tile numbers are handed out in chunks of consecutive tiles (32, or 16
+// for long segments), XCD x taking every eighth chunk (the kernel can also
+// give each XCD one contiguous run); the workgroups an XCD runs at once then
+// cover a few row tiles x feature tiles of one expert,
 // which share each weight tile and each row tile through that XCD's L2 (with
 // a plain feature-major order a large expert re-fetches its rows once per
 // feature tile). The grid covers the most tiles any routing can need,

@@ -183,14 +183,17 @@ hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 // of `features`: every (feature tile, row tile) pair the worst routing can
 // need, rounded up to a multiple of 8 (one run of tiles per XCD).
 // How tiles are dealt to the 8 XCDs: 0 = one contiguous run of tile numbers
-// per XCD; c > 0 = chunks of c consecutive tiles dealt round-robin. Long
-// segments (at least 512 rows per expert at full capacity) use chunks of 16:
-// each XCD then gets a share of every expert instead of a few whole
-// experts, which evens out the HBM traffic the XCDs draw (measured on
-// MI355X at 32768 tokens, 256 experts: 14.5 vs 15.2 ms); shorter segments
-// keep the runs (3.59 vs 3.64 ms at 4096 tokens).
+// per XCD; c > 0 = chunks of c consecutive tiles dealt round-robin. Dealt in
+// chunks, each XCD gets a share of every large expert instead of a few whole
+// experts, which evens out the HBM traffic the XCDs draw, while a chunk still
+// keeps a block of one expert's tiles together in one L2. Measured on MI355X
+// (256 experts, 7168 -> 4096, each box interleaved): long segments (at least
+// 512 rows per expert at full capacity; 32768 tokens) 14.5 ms with chunks of
+// 16 against 15.2 with runs, 32 within 0.5 % of 16 either way, 64 slower;
+// shorter segments (4096 tokens) 3.46-3.49 ms with chunks of 32 against
+// 3.54-3.56 with runs, 3.51 with 16, 3.59 with 64.
 inline int32_t gemm_xcd_chunk(int64_t max_rows, int32_t E) {
-    return max_rows >= int64_t(512) * E ? 16 : 0;
+    return max_rows >= int64_t(512) * E ? 16 : 32;
 }
 inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile,
                                  int32_t features) {
