@@ -137,6 +137,47 @@ def test_backward_full_shapes(name):
     _free()
 
 
+def test_backward_past_4_gib():
+    """40960 tokens of 14 KiB rows (327680 rows, 4.70 GB of dL/dy_e):
+    combine_backward writes and reads rows past byte offset 2^32 and
+    dispatch_backward gathers them (64-bit addressing). dL/dy_e and dL/dx
+    bitwise; dL/dscores within the fp32 dot-product bound on the tokens that
+    have a row past 4 GiB."""
+    w = workloads.Workload("past_4_gib", T=40960, ntpr=40960, nmax=40960, D=7168, E=256, K=8,
+                           dtype="bf16", routing="zipf", zipf_s=1.2, scores="sigmoid_norm",
+                           seed=3)
+    note("backward past 4 GiB: drawing inputs")
+    b = workloads.make_batch(w)
+    g = _grad_y(w.T, w.D, w.dtype, 77)
+    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV, backward=True)
+    note("backward past 4 GiB: GPU")
+    gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, w.T, w.ntpr)
+    del disp
+    _free()
+    note("backward past 4 GiB: oracle")
+    ob = oracle_backward(b["x"], b["ids"], b["scores"], g, w.T, w.ntpr, w.E, w.K)
+    row_bytes = w.D * 2
+    assert gb["total"] == ob["total"] and ob["total"] * row_bytes > 1 << 32
+    np.testing.assert_array_equal(gb["row_map"], ob["row_map"])
+    assert np.array_equal(gb["g_e"].view(np.uint8), ob["g_e"].view(np.uint8)), "dL/dy_e"
+    assert np.array_equal(gb["g_x"].view(np.uint8), ob["g_x"].view(np.uint8)), "dL/dx"
+    rm = ob["row_map"][:w.T].astype(np.int64)
+    far = np.nonzero((rm * row_bytes >= 1 << 32).any(axis=1))[0]
+    assert far.size > 0
+    tokens = far[:: max(1, far.size // 1024)]
+    gamma = w.D * U32 / (1 - w.D * U32)
+    G = _f64(g[tokens])
+    for k in range(w.K):
+        r = rm[tokens, k]
+        ok = r >= 0
+        mag = np.zeros(tokens.size)
+        mag[ok] = np.sum(np.abs(G[ok] * _f64(ob["x_e"][r[ok]])), axis=1)
+        err = np.abs(gb["g_s"][tokens, k].astype(np.float64) - ob["g_s"][tokens, k])
+        assert np.all(err <= gamma * mag + 1e-30), (k, float(err.max()))
+    del ob, gb
+    _free()
+
+
 def test_backward_unequal_counts_reproduce_equal_count_run():
     w, b, g, disp = _case("padded")
     note("backward padding invariance, full run")
