@@ -232,6 +232,57 @@ def test_grouped_gemm_dsv3_full_size_sampled():
     _free()
 
 
+def test_grouped_gemm_rows_past_4_gib():
+    """40960 tokens dispatched (327680 rows, 4.70 GB of x_e), experts
+    7168 -> 4096 with tiled weights: rows past byte offset 2^32 are read, and
+    output rows past 2^31 bytes written (64-bit addressing). Rows outside the
+    segments untouched; sampled outputs, most of them in rows past 4 GiB of
+    x_e, against the oracle's dot products within the fp32 bound."""
+    sh = workloads.EXPERT_SHAPES["dsv3"]
+    k_in, n_out = sh["k_in"], sh["n_out"]
+    wl = workloads.Workload("past_4_gib", T=40960, ntpr=40960, nmax=40960, D=k_in, E=256, K=8,
+                            dtype="bf16", routing="zipf", zipf_s=1.2, scores="sigmoid_norm",
+                            seed=3)
+    b = workloads.make_batch(wl)
+    note("past 4 GiB: expert weights")
+    w = workloads.expert_weights(wl.E, n_out, k_in, sh["seed"])
+    wt = tile_expert_weights(x_to_dev(w))
+    disp = MoeDispatcher(wl.nmax, wl.D, wl.E, wl.K, dtype=torch.bfloat16, device=DEV)
+    ids_d, s_d = i32_dev(b["ids"]), f32_dev(b["scores"])
+    note("past 4 GiB: layout + dispatch + grouped_gemm")
+    lay = disp.layout(ids_d, wl.ntpr)
+    dsp = disp.dispatch(x_to_dev(b["x"]), s_d, ids_d, lay.counts, num_tokens_per_rank=wl.ntpr)
+    max_rows = round_up4(wl.ntpr) * wl.K
+    out = torch.full((max_rows, n_out), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    grouped_gemm(dsp.x_e, wt, lay.offsets, out)
+    sync_or_fail(120)
+    total = int(lay.offsets[-1].item())
+    row_bytes = k_in * 2
+    assert total * row_bytes > 1 << 32
+    ov = out.view(torch.int16)
+    assert not bool((ov[:total] == -1).any()), "a row of the segments was not written"
+    assert bool((ov[total:] == -1).all()), "a row past the total was written"
+    got_off = lay.offsets.cpu().numpy()
+    del wt
+    lo = oracle.layout(b["ids"], wl.T, wl.ntpr, wl.E, wl.K)
+    x_e, _ = oracle.dispatch(b["x"], b["scores"], wl.K, lo["src"], ORACLE_THREADS)
+    off = lo["offsets"]
+    assert np.array_equal(got_off, off)
+    rng = np.random.default_rng(4)
+    far = (1 << 32) // row_bytes                       # first row past 4 GiB of x_e
+    rows = np.concatenate([rng.integers(far, total, 3000), rng.integers(0, far, 500),
+                           [far, total - 1]]).astype(np.int64)
+    cols = np.concatenate([rng.integers(0, n_out, 3500), [0, n_out - 1]]).astype(np.int64)
+    note(f"past 4 GiB: oracle at {rows.size} positions")
+    exact = oracle.grouped_gemm_at(x_e, w, off, rows, cols, ORACLE_THREADS)
+    owner = np.searchsorted(off, rows, side="right") - 1
+    mag = np.sum(np.abs(_f64(x_e[rows])) * np.abs(_f64(w[owner, cols])), axis=1)
+    got = x_to_np(out[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
+    _assert_within_bound(got, exact, mag, k_in, "rows past 4 GiB")
+    del disp, out, dsp
+    _free()
+
+
 def _identity_experts(E, D):
     c = 2.0 ** (np.arange(E) % 5 - 2)
     w = np.zeros((E, D, D), np.uint16)
