@@ -133,6 +133,41 @@ def test_prefill_layout_and_sampled_rows():
     _free()
 
 
+def test_rows_past_4_gib():
+    """40960 tokens of 14 KiB rows (327680 slots, 4.70 GB of x_e): the
+    ranking dispatch writes rows past byte offset 2^32. Layout, row map,
+    source map and scores against the separate calls and the oracle; sampled
+    rows, most of them past 4 GiB, bit for bit against x."""
+    w = workloads.Workload("past_4_gib", T=40960, ntpr=40960, nmax=40960, D=7168, E=256, K=8,
+                           dtype="bf16", routing="zipf", zipf_s=1.2, scores="sigmoid_norm",
+                           seed=3)
+    b = workloads.make_batch(w)
+    a = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV)
+    x_d, ids_d, s_d = x_to_dev(b["x"]), i32_dev(b["ids"]), f32_dev(b["scores"])
+    note("fused past 4 GiB: separate path")
+    lay = a.layout(ids_d, w.ntpr)
+    a.dispatch(x_d, s_d, ids_d, lay.counts, num_tokens_per_rank=w.ntpr)
+    sep = _read(a, w.ntpr, copy_x_e=False)
+    row_bytes = w.D * 2
+    assert sep["total"] * row_bytes > 1 << 32
+    far = (1 << 32) // row_bytes
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([rng.integers(far, sep["total"], 3000),
+                                     rng.integers(0, far, 500), [far, sep["total"] - 1]]))
+    a.x_e[:sep["total"]].view(torch.int16).fill_(-1)
+    a.row_map.fill_(-7)
+    note("fused past 4 GiB: fused path on the same context")
+    a.layout_dispatch(x_d, s_d, ids_d, num_tokens_per_rank=w.ntpr)
+    fused = _read(a, w.ntpr, copy_x_e=False)
+    _assert_same(sep, fused)
+    o = oracle.layout(b["ids"], w.T, w.ntpr, w.E, w.K)
+    assert_layout_equal(fused, o, w.T)
+    got = x_to_np(a.x_e[torch.from_numpy(rows).to(DEV)])
+    assert np.array_equal(got.view(np.uint8), b["x"][o["src"][rows] // w.K].view(np.uint8))
+    del a
+    _free()
+
+
 def test_empty_batch():
     K = 4
     ids = np.zeros((0, K), np.int32)
