@@ -114,8 +114,9 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
-// Layout fused into dispatch, two launches instead of three. The count
-// launch's last workgroup to finish (found with a per-context completion
+// Layout fused into dispatch, two launches (the separate calls take three
+// above kLayoutSingleMaxSlots slots, two up to it). The count launch's last
+// workgroup to finish (found with a per-context completion
 // counter, kept in a static device array so it starts at zero) turns the
 // tile histograms in block_hist into each tile's first row per expert and
 // writes counts and offsets; dispatch then ranks each of its tokens' slots

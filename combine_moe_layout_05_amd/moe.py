@@ -264,9 +264,9 @@ class MoeDispatcher:
     def layout_dispatch(self, x_TD: torch.Tensor, topk_scores_TK: torch.Tensor,
                         topk_expert_ids_TK: torch.Tensor, *,
                         num_tokens_per_rank: Optional[int] = None):
-        """layout() then dispatch() in two launches instead of three
-        (moe_layout_dispatch); same results bit for bit. Returns (Layout,
-        Dispatched)."""
+        """layout() then dispatch() in two launches (moe_layout_dispatch; the
+        separate calls take three above 32768 slots); same results bit for
+        bit. Returns (Layout, Dispatched)."""
         x = self._dev(x_TD, "x_TD", self.dtype, self.hidden)
         T = x.shape[0]
         s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)

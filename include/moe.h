@@ -177,8 +177,9 @@ int moe_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
                  const int32_t *d_topk_ids, const int32_t *d_counts, int32_t T,
                  int32_t num_tokens_per_rank, void *stream);
 
-/* moe_layout followed by moe_dispatch in two launches instead of three, with
- * the same results bit for bit: counts, offsets, row_map, src_map, x_e and
+/* moe_layout followed by moe_dispatch in two launches (the separate calls
+ * take three above 32768 slots, two up to it), with the same results bit for
+ * bit: counts, offsets, row_map, src_map, x_e and
  * s_e exactly as those two calls write them ([TT] "Backend behavior": the
  * fused-permute output is sized from the current capacity; [UC] "Internode"
  * 2 and 3: the counts and the total stay on the device). The count launch's
