@@ -117,14 +117,16 @@ static int32_t orc_expert_of(const int32_t *ids, int64_t T, int32_t E,
  *   row_map[t*K+k] = row of slot (t,k) in the expert-major buffer, -1 for
  *                  no expert, for every t < round_up4(ntpr)
  *   src[row]     = t*K + k of the slot stored at that row, rows [0,total)
- * Returns total, or -1 if the capacity relation fails.
+ * Returns total, or -1 if 0 <= T <= ntpr fails ([TT] "API design").
  */
 int64_t orc_layout(const int32_t *ids, int64_t T, int64_t ntpr, int32_t E,
                    int32_t K, int32_t *counts, int32_t *offsets,
                    int32_t *row_map, int32_t *src)
 {
     if (E < 1 || K < 1) return -1;
-    if (T < 0 || ntpr < 0 || T > orc_round_up4(ntpr)) return -1;
+    /* [TT] "API design": T <= num_tokens_per_rank; the padding of [NA]
+     * "Fix" only adds rows past ntpr, it never admits more tokens. */
+    if (T < 0 || ntpr < 0 || T > ntpr) return -1;
     int64_t n = orc_round_up4(ntpr) * K;
 
     for (int32_t e = 0; e < E; ++e) counts[e] = 0;

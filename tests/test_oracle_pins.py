@@ -121,6 +121,33 @@ def test_capacity_relation_cases():
     assert oracle.round_up4(a) == a and oracle.round_up4(b) == b
 
 
+def test_layout_rejects_more_tokens_than_the_capacity():
+    """The page's relation is T <= num_tokens_per_rank; rounding the capacity
+    up to 4 adds padding rows, not room for tokens. So the layout must reject
+    ntpr < T <= round_up4(ntpr) as check_capacity does, at its C entry point
+    and through the wrapper, and still accept T == ntpr."""
+    import ctypes as C
+    E, K = 8, 2
+    from oracle.oracle import _load
+    lib = _load()
+    for ntpr in (1, 2, 3, 5, 6, 7, 2045, 2046, 2047):
+        n4 = oracle.round_up4(ntpr)
+        for T in range(ntpr + 1, n4 + 1):
+            assert oracle.check_capacity(T, ntpr, 4096) != 0
+            ids = _routing(T, E, K, seed=T)
+            counts = np.zeros(E, np.int32)
+            offsets = np.zeros(E + 1, np.int32)
+            row_map = np.empty(n4 * K, np.int32)
+            src = np.empty(n4 * K, np.int32)
+            p = lambda a: a.ctypes.data_as(C.c_void_p)  # noqa: E731
+            assert lib.orc_layout(p(ids), T, ntpr, E, K, p(counts), p(offsets), p(row_map),
+                                  p(src)) == -1
+            with pytest.raises(ValueError):
+                oracle.layout(ids, T, ntpr, E, K)
+        ids = _routing(ntpr, E, K, seed=ntpr)
+        assert oracle.layout(ids, ntpr, ntpr, E, K)["total"] == ntpr * K
+
+
 # --------------------------------------------------------------------------
 # Layout
 
