@@ -68,8 +68,8 @@ SIGNATURES = {
     "moe_layout_dispatch": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "moe_topk_from_routing_map": (_int, [_vp, _vp, _vp, _i32, _vp, C.POINTER(_vp),
                                          C.POINTER(_vp), C.POINTER(_vp)]),
-    "moe_combine_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp),
-                                    C.POINTER(_vp)]),
+    "moe_combine_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                                    C.POINTER(_vp), C.POINTER(_vp)]),
     "moe_dispatch_backward": (_int, [_vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
     "moe_grouped_gemm": (_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _i32, _i32, _vp]),
     "moe_tiled_weights_bytes": (_i64, [_i32, _i32, _i32]),

@@ -8,7 +8,10 @@
 //                                             the element type
 //   dL/ds[t][k]     = <dL/dy[t], y_e[r(t,k)]> fp32 fused multiply-adds
 // for every slot with an expert; a no-expert slot gets dL/ds = +0.0 and no
-// row. Rows of dL/dy_e past the true total are not written.
+// row. Rows of dL/dy_e from the true total up to the current capacity's last
+// row reached no token, so their gradient is +0.0; with a device pointer to
+// that total they are written as such (the total stays on the device:
+// "ep: graph-safe worst-token HT dispatch+combine", "Internode" item 3).
 //
 // One workgroup per token, W = ceil(chunks/64) wavefronts (at most 16): each
 // lane owns 16-byte chunks lane + 64*wave + 64*W*i of the row, so the
@@ -18,7 +21,9 @@
 // in element order within a lane, then a fixed butterfly over the 64 lanes,
 // then the wavefronts in order. The reduction order is fixed, so results are
 // deterministic; it differs from plain left-to-right order, which stays
-// within the fp32 summation error bound of the dot product.
+// within the fp32 summation error bound of the dot product. The launch has
+// kTailBlocks more workgroups than tokens; they store zeros into the rows
+// [*total_rows, row_limit), a row per workgroup per turn.
 #include "moe_kernels.h"
 #include "moe_lanes.h"
 
@@ -27,13 +32,16 @@
 namespace moe {
 namespace {
 
+// Workgroups of the launch that zero the rows past the true total.
+constexpr int32_t kTailBlocks = 512;
+
 template <int K, bool BF16>
 __global__ __launch_bounds__(kMaxBlockThreads)
 void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restrict__ y_e,
                              const int32_t* __restrict__ row_map,
-                             const float* __restrict__ scores, int32_t chunks,
-                             int64_t row_limit, v4i* __restrict__ grad_y_e,
-                             float* __restrict__ grad_s) {
+                             const float* __restrict__ scores, int32_t T, int32_t chunks,
+                             int64_t row_limit, const int32_t* __restrict__ total_rows,
+                             v4i* __restrict__ grad_y_e, float* __restrict__ grad_s) {
     using L = Lanes<BF16>;
     __shared__ int32_t tok_rows[K];
     __shared__ float tok_scores[K];
@@ -43,6 +51,21 @@ void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restri
     const int wave = tid >> 6;
     const int waves = static_cast<int>(blockDim.x) >> 6;
     const int64_t t = blockIdx.x;
+
+    if (t >= T) {
+        // Rows [total, row_limit) were reached by no slot. The total is
+        // clamped to [0, row_limit], so a wrong value cannot move the stores
+        // outside the current capacity's rows.
+        if (!total_rows) return;
+        int64_t lo = *total_rows;
+        lo = lo < 0 ? 0 : (lo > row_limit ? row_limit : lo);
+        const v4i zero = {0, 0, 0, 0};
+        for (int64_t r = lo + (t - T); r < row_limit; r += kTailBlocks) {
+            v4i* dst = grad_y_e + r * chunks;
+            for (int32_t c = tid; c < chunks; c += static_cast<int32_t>(blockDim.x)) dst[c] = zero;
+        }
+        return;
+    }
 
     if (tid < K) {
         const int32_t r = row_map[t * K + tid];
@@ -117,10 +140,12 @@ template <int K, bool BF16>
 hipError_t launch_k(const CombineBackwardArgs& a, hipStream_t stream) {
     int32_t waves = (a.chunks + 63) / 64;
     if (waves > kMaxBlockWaves) waves = kMaxBlockWaves;
-    hipLaunchKernelGGL((combine_backward_kernel<K, BF16>), dim3(static_cast<uint32_t>(a.T)),
+    // Token workgroups first, then the tail workgroups (only when asked for).
+    const int64_t blocks = int64_t(a.T) + (a.total_rows ? kTailBlocks : 0);
+    hipLaunchKernelGGL((combine_backward_kernel<K, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(64 * waves), 0, stream, static_cast<const v4i*>(a.grad_y),
-                       static_cast<const v4i*>(a.y_e), a.row_map, a.scores, a.chunks,
-                       a.row_limit, static_cast<v4i*>(a.grad_y_e), a.grad_s);
+                       static_cast<const v4i*>(a.y_e), a.row_map, a.scores, a.T, a.chunks,
+                       a.row_limit, a.total_rows, static_cast<v4i*>(a.grad_y_e), a.grad_s);
     return hipGetLastError();
 }
 
@@ -141,7 +166,7 @@ hipError_t launch_dtype(const CombineBackwardArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t stream) {
-    if (a.T <= 0) return hipSuccess;
+    if (a.T <= 0 && !a.total_rows) return hipSuccess;
     return a.bf16 ? launch_dtype<true>(a, stream) : launch_dtype<false>(a, stream);
 }
 

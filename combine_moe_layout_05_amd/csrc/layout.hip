@@ -601,8 +601,7 @@ hipError_t launch_single_r(const LayoutArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    const bool single = a.launches == 1 || (a.launches == 0 && a.nslots <= kLayoutSingleMaxSlots);
-    if (single) {
+    if (layout_single_launch(a.nslots, a.launches)) {
         switch (layout_single_slots_per_lane(a.nslots)) {
             case 1: return launch_single_r<1>(a, stream);
             case 2: return launch_single_r<2>(a, stream);

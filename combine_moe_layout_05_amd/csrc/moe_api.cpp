@@ -457,8 +457,9 @@ int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
 }
 
 int moe_combine_backward(moe_ctx* ctx, const void* d_grad_y, const void* d_y_expert,
-                         const int32_t* d_row_map, const float* d_scores, int32_t T, int32_t ntpr,
-                         void* stream, void** d_grad_y_expert_out, float** d_grad_scores_out) {
+                         const int32_t* d_row_map, const float* d_scores, const int32_t* d_total,
+                         int32_t T, int32_t ntpr, void* stream, void** d_grad_y_expert_out,
+                         float** d_grad_scores_out) {
     if (!ctx || !d_grad_y_expert_out || !d_grad_scores_out) return MOE_ERR_INVALID_ARG;
     if (!(ctx->cfg.flags & MOE_FLAG_BACKWARD)) return MOE_ERR_UNSUPPORTED;
     int64_t ntpr4 = 0;
@@ -480,6 +481,7 @@ int moe_combine_backward(moe_ctx* ctx, const void* d_grad_y, const void* d_y_exp
     a.bf16 = ctx->cfg.dtype == MOE_BF16;
     a.grad_y_e = at<void>(ctx, ctx->desc.g_e);
     a.grad_s = at<float>(ctx, ctx->desc.g_s);
+    a.total_rows = d_total;
     if (moe::launch_combine_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     *d_grad_y_expert_out = a.grad_y_e;

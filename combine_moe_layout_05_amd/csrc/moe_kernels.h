@@ -66,6 +66,18 @@ static_assert(kMaxExperts <= kLayoutSingleThreads, "one expert per thread in the
 // histograms, so rows can be read as 16-byte vectors.
 inline int32_t padded_experts(int32_t E) { return (E + 3) & ~3; }
 
+// Whether a layout of nslots slots runs as the single launch: forced by
+// launches (1: single, 2: two launches) or, with 0, chosen by size.
+inline bool layout_single_launch(int64_t nslots, int32_t launches) {
+    return launches == 1 || (launches == 0 && nslots <= kLayoutSingleMaxSlots);
+}
+// Bytes of per-tile histograms (block_hist) such a layout uses: none for the
+// single launch, one row of round_up4(E) int32 per tile for the two launches.
+inline int64_t layout_hist_bytes(int64_t nslots, int32_t E, int32_t launches) {
+    if (layout_single_launch(nslots, launches)) return 0;
+    return layout_tiles(nslots, layout_slots_per_lane(nslots)) * padded_experts(E) * 4;
+}
+
 // Bits needed to tell experts 0..E-1 apart (0 for E == 1).
 inline int expert_bits(int32_t E) {
     int b = 0;
@@ -164,6 +176,8 @@ struct CombineBackwardArgs {
     bool bf16;
     void* grad_y_e;         // rows r(t,k) written
     float* grad_s;          // [T][K]
+    const int32_t* total_rows = nullptr;  // device; rows [*total_rows, row_limit) of
+                                          // grad_y_e get +0.0 (nullptr: not written)
 };
 hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t stream);
 

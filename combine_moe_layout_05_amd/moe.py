@@ -144,6 +144,13 @@ class MoeDispatcher:
     The workspace (a uint8 device tensor) is allocated once here, at the
     lifetime maximum, and carved by the library into fixed-address buffers;
     no later call allocates, grows, synchronizes or reads back.
+
+    x_e_generation counts the calls that rewrote x_e (dispatch,
+    dispatch_scaled, layout_dispatch), so a holder of an x_e view can tell
+    whether the rows it saw are still there. close() (also run when the
+    object is collected) waits for the device's queued work before the
+    library context is destroyed, since that work may still use the context's
+    buffers and counter slot.
     """
 
     def __init__(self, num_max_tokens_per_rank: int, hidden: int, num_experts: int,
@@ -161,6 +168,7 @@ class MoeDispatcher:
         self.hidden, self.num_experts, self.topk = hidden, num_experts, topk
         self.num_max_tokens_per_rank = num_max_tokens_per_rank
         self.backward_enabled = bool(backward)
+        self.x_e_generation = 0
         self._cfg = L.MoeConfig(num_max_tokens_per_rank, hidden, num_experts, topk,
                                 _DTYPES[dtype], L.MOE_FLAG_BACKWARD if backward else 0)
         nbytes = C.c_size_t(0)
@@ -196,11 +204,29 @@ class MoeDispatcher:
         nbytes = int(n) * torch.empty(0, dtype=dtype).element_size()
         return self.workspace[int(off):int(off) + nbytes].view(dtype)
 
-    def __del__(self):
+    def rows_for(self, num_tokens_per_rank: int) -> int:
+        """Rows of the expert-major buffers a call with this capacity uses."""
+        return round_up4(int(num_tokens_per_rank)) * self.topk
+
+    def close(self) -> None:
+        """Destroy the library context after the device has finished every
+        queued kernel (they may still read its buffers or hold its counter
+        slot). The workspace tensor is released with this object."""
         ctx = getattr(self, "_ctx", None)
         if ctx is not None and ctx.value:
+            if torch.cuda.is_current_stream_capturing():
+                # A wait is not allowed while a graph is being captured, and
+                # the captured work may use this context: keep it alive.
+                return
+            torch.cuda.synchronize(self.device)
             self._lib.moe_destroy(ctx)
             self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown: the runtime may be gone
+            pass
 
     # -- argument checks (marshalling) -------------------------------------
     def _dev(self, t: torch.Tensor, name: str, dtype: torch.dtype, cols: int) -> torch.Tensor:
@@ -258,6 +284,7 @@ class MoeDispatcher:
         ntpr = self._ntpr(T, num_tokens_per_rank)
         L.check(fn(self._ctx, x.data_ptr(), s.data_ptr(), ids.data_ptr(), counts.data_ptr(), T,
                    ntpr, _stream(self.device)), what)
+        self.x_e_generation += 1
         rows = round_up4(ntpr) * self.topk
         return Dispatched(self.x_e[:rows], self.s_e[:rows])
 
@@ -277,6 +304,7 @@ class MoeDispatcher:
         L.check(self._lib.moe_layout_dispatch(self._ctx, x.data_ptr(), s.data_ptr(),
                                               ids.data_ptr(), T, ntpr, _stream(self.device)),
                 "moe_layout_dispatch")
+        self.x_e_generation += 1
         n4 = round_up4(ntpr)
         rows = n4 * self.topk
         return (Layout(self.counts, self.offsets, self.row_map[:n4]),
@@ -350,9 +378,14 @@ class MoeDispatcher:
 
     def combine_backward(self, grad_y: torch.Tensor, y_expert: torch.Tensor,
                          row_map: torch.Tensor, topk_scores_TK: torch.Tensor, *,
-                         num_tokens_per_rank: Optional[int] = None):
-        """(dL/dy_expert [round_up4(ntpr)*K, D] view, rows [0,total) valid;
-        dL/dscores [T, K] view) for dL/dy = grad_y [T, D]."""
+                         num_tokens_per_rank: Optional[int] = None,
+                         total: Optional[torch.Tensor] = None):
+        """(dL/dy_expert [round_up4(ntpr)*K, D] view; dL/dscores [T, K] view)
+        for dL/dy = grad_y [T, D]. Rows [0, total) of dL/dy_expert are the
+        slots' rows. With `total` (a one-element int32 device tensor holding
+        the layout's offsets[E], e.g. Layout.offsets[-1:]) the library also
+        writes +0.0 into the rows from *total on, which no slot reaches;
+        otherwise those rows keep what the buffer held."""
         s = self._dev(topk_scores_TK, "topk_scores_TK", torch.float32, self.topk)
         T = s.shape[0]
         g = self._dev(grad_y, "grad_y", self.dtype, self.hidden)
@@ -361,9 +394,15 @@ class MoeDispatcher:
         ntpr = self._ntpr(T, num_tokens_per_rank)
         ye = self._expert_rows(y_expert, "y_expert", ntpr)
         rm = self._row_map(row_map, T)
+        tot_ptr = 0
+        if total is not None:
+            if (total.device != self.device or total.dtype != torch.int32
+                    or total.numel() != 1 or not total.is_contiguous()):
+                raise ValueError("total must be a one-element int32 tensor on the device")
+            tot_ptr = total.data_ptr()
         out_e, out_s = C.c_void_p(), C.c_void_p()
         L.check(self._lib.moe_combine_backward(self._ctx, g.data_ptr(), ye.data_ptr(),
-                                               rm.data_ptr(), s.data_ptr(), T, ntpr,
+                                               rm.data_ptr(), s.data_ptr(), tot_ptr, T, ntpr,
                                                _stream(self.device), C.byref(out_e),
                                                C.byref(out_s)), "moe_combine_backward")
         return self.g_e[:round_up4(ntpr) * self.topk], self.g_s[:T]

@@ -259,20 +259,28 @@ int moe_combine(moe_ctx *ctx, const void *d_y_expert, const int32_t *d_row_map,
  *   g_e[r]       = scores[t][k] * d_grad_y[t]   (one fp32 product, rounded to
  *                                               the element type)
  *   g_s[t][k]    = <d_grad_y[t], d_y_expert[r]> (fp32, fixed reduction order)
- * and g_s[t][k] = +0.0 for a slot without an expert. Rows of g_e other than
- * the slots' rows are not written.
+ * and g_s[t][k] = +0.0 for a slot without an expert. With d_total, the rows
+ * g_e[*d_total .. round_up4(num_tokens_per_rank) * K) are set to +0.0: no slot
+ * reaches them, so their gradient is zero (*d_total is read on the device,
+ * clamped to [0, round_up4(num_tokens_per_rank) * K]; [UC] "Internode" 3:
+ * the true total stays on the device). Other rows of g_e are not written.
  *   d_grad_y       [T][D] gradient of the combine output
  *   d_y_expert     the expert outputs the forward combine read,
  *                  [>= round_up4(num_tokens_per_rank) * K][D]
  *   d_row_map, d_topk_scores, T, num_tokens_per_rank: as for moe_combine
  *                  (the same MOE_ERR_STATE rule for the context's row map)
+ *   d_total        int32 in device memory: the number of rows the slots of
+ *                  d_row_map reach (offsets[E] of the layout that made it,
+ *                  e.g. the context's offsets + E, or a copy of it), or NULL
+ *                  to leave the rows past the slots' rows unwritten
  *   *d_grad_y_expert_out  receives the address of g_e ([nmax4*K][D])
  *   *d_grad_scores_out    receives the address of g_s ([nmax4][K]; rows [0,T))
  * Needs MOE_FLAG_BACKWARD (MOE_ERR_UNSUPPORTED otherwise). */
 int moe_combine_backward(moe_ctx *ctx, const void *d_grad_y, const void *d_y_expert,
-                         const int32_t *d_row_map, const float *d_topk_scores, int32_t T,
-                         int32_t num_tokens_per_rank, void *stream,
-                         void **d_grad_y_expert_out, float **d_grad_scores_out);
+                         const int32_t *d_row_map, const float *d_topk_scores,
+                         const int32_t *d_total, int32_t T, int32_t num_tokens_per_rank,
+                         void *stream, void **d_grad_y_expert_out,
+                         float **d_grad_scores_out);
 
 /* Backward of moe_dispatch: for t < T,
  *   g_x[t] = sum over k = 0..K-1 with d_row_map[t][k] >= 0 of

@@ -63,8 +63,11 @@ static void one_config(int32_t nmax, int32_t D, int32_t E, int32_t K, int32_t dt
         void *ge = nullptr, *gx = nullptr;
         float* gs = nullptr;
         const int want = (flags & MOE_FLAG_BACKWARD) ? MOE_OK : MOE_ERR_UNSUPPORTED;
-        EXPECT(moe_combine_backward(ctx, p, p, row_map, static_cast<const float*>(p), T, ntpr,
-                                    nullptr, &ge, &gs) == want);
+        EXPECT(moe_combine_backward(ctx, p, p, row_map, static_cast<const float*>(p), nullptr,
+                                    T, ntpr, nullptr, &ge, &gs) == want);
+        EXPECT(moe_combine_backward(ctx, p, p, row_map, static_cast<const float*>(p),
+                                    static_cast<const int32_t*>(p), T, ntpr, nullptr, &ge,
+                                    &gs) == want);
         EXPECT(moe_dispatch_backward(ctx, p, row_map, T, ntpr, nullptr, &gx) == want);
         int32_t *ids = nullptr, *nexp = nullptr;
         float* sc = nullptr;
@@ -150,6 +153,7 @@ int main() {
     EXPECT(moe_validate_num_max(100, 99) == MOE_OK && moe_validate_num_max(0, 0) != MOE_OK);
     EXPECT(moe_check_capacity(3, 4, 8) == MOE_OK && moe_check_capacity(5, 4, 8) != MOE_OK);
     for (int s = -7; s <= 0; ++s) EXPECT(moe_strerror(s) != nullptr);
+
 
     // expert step
     void* p = fake(uintptr_t(1) << 41);

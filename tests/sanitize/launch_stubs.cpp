@@ -22,9 +22,13 @@ static void require(bool ok, const char* what) {
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t) {
     require(a.E >= 1 && a.nvalid >= 0 && a.nslots >= a.nvalid, "layout sizes");
     require(a.launches >= 0 && a.launches <= 2, "layout launches");
+    // The two-launch form needs its per-tile histograms.
+    require(layout_hist_bytes(a.nslots, a.E, a.launches) == 0 || a.block_hist != nullptr,
+            "layout histograms");
     ++g_launches;
     return hipSuccess;
 }
+
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t) {
     require(a.T >= 0 && a.K >= 1 && a.chunks >= 1 && a.segments >= 1 && a.block_waves >= 1 &&
                 a.block_waves <= kMaxBlockWaves,

@@ -19,7 +19,8 @@ import oracle
 import workloads
 from combine_moe_layout_05_amd import MoeDispatcher, MoeError, round_up4
 
-from gpu_util import DEV, ORACLE_THREADS, f32_dev, i32_dev, note, x_to_dev, x_to_np
+from gpu_util import (DEV, ORACLE_THREADS, f32_dev, i32_dev, note, sync_or_fail, x_to_dev,
+                      x_to_np)
 
 pytestmark = pytest.mark.gpu
 U32 = 2.0 ** -24
@@ -51,7 +52,7 @@ def gpu_backward(disp, x, ids, scores, g, T, ntpr):
     g_e, g_s = disp.combine_backward(x_to_dev(g[:T]), dsp.x_e, lay.row_map, s_d,
                                      num_tokens_per_rank=ntpr)
     g_x = disp.dispatch_backward(g_e, lay.row_map, T, num_tokens_per_rank=ntpr)
-    torch.cuda.synchronize()
+    sync_or_fail()
     total = int(lay.offsets[-1].item())
     return {"g_e": x_to_np(g_e[:total]), "g_s": g_s.cpu().numpy(), "g_x": x_to_np(g_x),
             "row_map": lay.row_map.cpu().numpy(), "total": total}
@@ -242,7 +243,7 @@ def test_backward_poisoned_workspace_and_flag():
     g = _grad_y(2048, w.D, "bf16", 8)
     disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV, backward=True)
     disp.workspace.fill_(0xFF)
-    torch.cuda.synchronize()
+    sync_or_fail()
     T = 614
     note("backward poison T=614")
     gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, T, w.ntpr)
@@ -259,5 +260,46 @@ def test_backward_poisoned_workspace_and_flag():
         plain.g_e
     with pytest.raises(MoeError):
         plain.dispatch_backward(plain.x_e, lay.row_map, 4)
-    torch.cuda.synchronize()
+    sync_or_fail()
+    _free()
+
+
+@pytest.mark.parametrize("T", [614, 2047, 0])
+def test_backward_total_zeroes_the_rows_no_slot_reaches(T):
+    """With the device-side total, moe_combine_backward writes +0.0 into the
+    dL/dy_e rows [total, round_up4(ntpr) * K), which no slot reaches, and
+    leaves the rows past the current capacity alone (a poisoned workspace
+    shows both). The slots' rows stay bitwise equal to the oracle."""
+    w = workloads.WORKLOADS["padded"]
+    b = workloads.make_batch(w)
+    g = _grad_y(2048, w.D, "bf16", 8)
+    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV, backward=True)
+    disp.workspace.fill_(0xFF)
+    sync_or_fail()
+    note(f"backward with total, poisoned workspace, T={T}")
+    ids_d, s_d = i32_dev(b["ids"][:T]), f32_dev(b["scores"][:T])
+    x_d = x_to_dev(b["x"][:T]) if T else torch.empty((0, w.D), dtype=torch.bfloat16, device=DEV)
+    g_d = x_to_dev(g[:T]) if T else torch.empty((0, w.D), dtype=torch.bfloat16, device=DEV)
+    lay = disp.layout(ids_d, w.ntpr)
+    dsp = disp.dispatch(x_d, s_d, ids_d, lay.counts, num_tokens_per_rank=w.ntpr)
+    total_d = lay.offsets[-1:].clone()
+    g_e, _ = disp.combine_backward(g_d, dsp.x_e, lay.row_map, s_d, num_tokens_per_rank=w.ntpr,
+                                   total=total_d)
+    sync_or_fail()
+    rows = round_up4(w.ntpr) * w.K
+    total = int(total_d.item())
+    assert g_e.shape[0] == rows
+    ob = oracle_backward(b["x"], b["ids"], b["scores"], g, T, w.ntpr, w.E, w.K) if T else None
+    if T:
+        assert total == ob["total"]
+        assert np.array_equal(x_to_np(g_e[:total]).view(np.uint8), ob["g_e"].view(np.uint8))
+    else:
+        assert total == 0
+    tail = g_e[total:rows].view(torch.int16)
+    assert bool((tail == 0).all()), "rows past the total must be exactly +0.0"
+    assert bool((disp.g_e[rows:].view(torch.int16) == -1).all()), "rows past the capacity"
+    with pytest.raises(ValueError):
+        disp.combine_backward(g_d, dsp.x_e, lay.row_map, s_d, num_tokens_per_rank=w.ntpr,
+                              total=lay.offsets)              # not a one-element tensor
+    del disp
     _free()

@@ -15,7 +15,7 @@ import workloads
 from combine_moe_layout_05_amd import MoeDispatcher, round_up4
 
 from gpu_util import (DEV, ORACLE_THREADS, assert_dispatch_equal, assert_layout_equal, f32_dev,
-                      i32_dev, note, torch_dtype, x_to_dev, x_to_np)
+                      i32_dev, note, sync_or_fail, torch_dtype, x_to_dev, x_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def _free():
 
 
 def _read(disp, ntpr, copy_x_e=True):
-    torch.cuda.synchronize()
+    sync_or_fail()
     total = int(disp.offsets[-1].item())
     n4 = round_up4(ntpr)
     out = {"counts": disp.counts.cpu().numpy(), "offsets": disp.offsets.cpu().numpy(),
@@ -273,7 +273,7 @@ def test_graph_replays_with_fresh_routing():
         lay, dsp = disp.layout_dispatch(x_d, s_d, ids_d)
         disp.combine(dsp.x_e, lay.row_map, s_d)
     torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
+    sync_or_fail()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         lay, dsp = disp.layout_dispatch(x_d, s_d, ids_d)
@@ -282,7 +282,7 @@ def test_graph_replays_with_fresh_routing():
         note(f"fused graph replay {i} T={T}")
         fill(T)
         g.replay()
-        torch.cuda.synchronize()
+        sync_or_fail()
         got = _read(disp, N)
         y_got = x_to_np(y)
         rl = ref.layout(ids_d, N)
@@ -346,3 +346,40 @@ def test_expert_counts_off_the_quad_grid(E):
     ids[rng.random((T, K)) < 0.03] = -1
     _check(_x(rng, T, 64, "bf16"), ids, rng.random((T, K)).astype(np.float32),
            T, T, T, 64, E, K, "bf16")
+
+
+def test_dropping_a_dispatcher_waits_for_its_queued_work():
+    """A fused call enqueued on a side stream, the dispatcher dropped right
+    after, a new dispatcher created (it takes the lowest free completion-
+    counter slot, the one just given back) and a fused call on the main
+    stream. Dropping waits for the queued work, so the two launches never
+    share a live counter: the side-stream results read before the drop and
+    the main-stream results both equal the oracle."""
+    w = workloads.WORKLOADS["graph"]
+    b = workloads.make_batch(w)
+    T = w.T
+    ids_d, s_d, x_d = i32_dev(b["ids"]), f32_dev(b["scores"]), x_to_dev(b["x"])
+    o = oracle.layout(b["ids"], T, w.ntpr, w.E, w.K)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    first = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV)
+    note("fused call on a side stream, then the dispatcher is dropped")
+    with torch.cuda.stream(side):
+        first.layout_dispatch(x_d, s_d, ids_d)
+        row_map_1 = first.row_map[:w.ntpr].clone()
+        offsets_1 = first.offsets.clone()
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    del first
+    gc.collect()
+    second = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV)
+    note("fused call on the main stream with a new dispatcher")
+    second.layout_dispatch(x_d, s_d, ids_d)
+    got = _read(second, w.ntpr, copy_x_e=False)
+    np.testing.assert_array_equal(row_map_1.cpu().numpy(), o["row_map"])
+    np.testing.assert_array_equal(offsets_1.cpu().numpy(), o["offsets"])
+    assert_layout_equal(got, o, T)
+    second.close()
+    with pytest.raises(Exception):
+        second.layout(ids_d)                   # a closed dispatcher has no context
+    del second
+    _free()

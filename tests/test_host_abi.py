@@ -170,20 +170,20 @@ def test_backward_calls_need_the_flag_and_a_matching_layout(lib):
     out_e, out_s, out_x = C.c_void_p(), C.c_void_p(), C.c_void_p()
     p = 1 << 41
     ctx, d, _ = _ctx(lib, _cfg(4096, 2048, 128, 8, L.MOE_BF16))
-    assert lib.moe_combine_backward(ctx, p, p, p, p, 5, 8, None, C.byref(out_e),
+    assert lib.moe_combine_backward(ctx, p, p, p, p, None, 5, 8, None, C.byref(out_e),
                                     C.byref(out_s)) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_dispatch_backward(ctx, p, p, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_UNSUPPORTED
     lib.moe_destroy(ctx)
     ctx, d, _ = _ctx(lib, _cfg(4096, 2048, 128, 8, L.MOE_BF16, L.MOE_FLAG_BACKWARD))
     rm = (1 << 40) + d.row_map
-    assert lib.moe_combine_backward(ctx, p, p, rm, p, 5, 8, None, C.byref(out_e),
+    assert lib.moe_combine_backward(ctx, p, p, rm, p, p, 5, 8, None, C.byref(out_e),
                                     C.byref(out_s)) == L.MOE_ERR_STATE
     assert lib.moe_dispatch_backward(ctx, p, rm, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_STATE
-    assert lib.moe_combine_backward(ctx, p, p, p, p, 9, 8, None, C.byref(out_e),
+    assert lib.moe_combine_backward(ctx, p, p, p, p, p, 9, 8, None, C.byref(out_e),
                                     C.byref(out_s)) == L.MOE_ERR_CAPACITY
-    assert lib.moe_combine_backward(ctx, None, p, p, p, 5, 8, None, C.byref(out_e),
+    assert lib.moe_combine_backward(ctx, None, p, p, p, p, 5, 8, None, C.byref(out_e),
                                     C.byref(out_s)) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_combine_backward(ctx, p, p, p, p, 5, 8, None, None,
+    assert lib.moe_combine_backward(ctx, p, p, p, p, None, 5, 8, None, None,
                                     C.byref(out_s)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(ctx, None, p, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(ctx, p, p, 5, 4097, None, C.byref(out_x)) == L.MOE_ERR_CAPACITY
@@ -339,3 +339,4 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "moe_oracle" not in text and "liborc" not in text, f
+
