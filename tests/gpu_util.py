@@ -66,7 +66,7 @@ def run_gpu(disp, x, ids, scores, T, ntpr, y_expert=None, copy_x_e=True):
     dsp = disp.dispatch(x_d, s_d, ids_d, lay.counts, num_tokens_per_rank=ntpr)
     ye = dsp.x_e if y_expert is None else y_expert
     y = disp.combine(ye, lay.row_map, s_d, num_tokens_per_rank=ntpr)
-    torch.cuda.synchronize()
+    sync_or_fail()
     total = int(lay.offsets[-1].item())
     out = {
         "counts": lay.counts.cpu().numpy(),

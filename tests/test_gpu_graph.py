@@ -47,11 +47,11 @@ class Captured:
         with torch.cuda.stream(side):          # warm-up outside the capture
             self._body()
         torch.cuda.current_stream(DEV).wait_stream(side)
-        torch.cuda.synchronize()
+        sync_or_fail()
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
             self.y = self._body()
-        torch.cuda.synchronize()
+        sync_or_fail()
         self.eager_calls = 0
 
     def _body(self):
@@ -77,7 +77,7 @@ class Captured:
         d.dispatch(x_to_dev(x[:T]), s_d, ids_d, lay.counts, num_tokens_per_rank=ntpr)
         ye = d.x_e[: lay.row_map.shape[0] * W.K] * 2
         y = d.combine(ye, lay.row_map, s_d, num_tokens_per_rank=ntpr)
-        torch.cuda.synchronize()
+        sync_or_fail()
         self.eager_calls += 1
         return x_to_np(y), lay.counts.cpu().numpy(), lay.offsets.cpu().numpy()
 
@@ -201,11 +201,11 @@ def test_graph_buckets_with_different_capacities_share_one_context():
         with torch.cuda.stream(side):
             body()
         torch.cuda.current_stream(DEV).wait_stream(side)
-        torch.cuda.synchronize()
+        sync_or_fail()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             outs = body()
-        torch.cuda.synchronize()
+        sync_or_fail()
         graphs[n] = (g, st, outs)
 
     rng = np.random.default_rng(31)

@@ -13,7 +13,7 @@ import oracle
 import workloads
 from combine_moe_layout_05_amd import MoeDispatcher, round_up4
 
-from gpu_util import DEV, i32_dev, note
+from gpu_util import DEV, i32_dev, note, sync_or_fail
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def _ids(T, E, K, routing, s, seed, bad=False, dup=False):
 def _run(disp, ids_np, T, ntpr, launches):
     disp.set_tuning(layout_launches=launches)
     lay = disp.layout(i32_dev(ids_np), ntpr)
-    torch.cuda.synchronize()
+    sync_or_fail()
     total = int(lay.offsets[-1].item())
     return {"counts": lay.counts.cpu().numpy().copy(), "offsets": lay.offsets.cpu().numpy().copy(),
             "row_map": lay.row_map.cpu().numpy().copy(),

@@ -13,8 +13,8 @@ import workloads
 from combine_moe_layout_05_amd import MoeDispatcher, MoeError, round_up4
 
 from gpu_util import (DEV, ORACLE_THREADS, assert_combine_within_bar, assert_dispatch_equal,
-                      assert_layout_equal, f32_dev, i32_dev, note, run_gpu, torch_dtype,
-                      x_to_dev, x_to_np)
+                      assert_layout_equal, f32_dev, i32_dev, note, run_gpu, sync_or_fail,
+                      torch_dtype, x_to_dev, x_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -222,7 +222,7 @@ def test_poisoned_workspace(name, T):
     b = workloads.make_batch(w)
     disp = _dispatcher(w)
     disp.workspace.fill_(0xFF)                 # NaN for floats, -1 for int32
-    torch.cuda.synchronize()
+    sync_or_fail()
     ntpr = w.ntpr
     note(f"poison {name} T={T}")
     g = run_gpu(disp, b["x"], b["ids"], b["scores"], T, ntpr)
@@ -382,7 +382,7 @@ def test_non_identity_expert_output():
     dsp = disp.dispatch(x_to_dev(b["x"][:T]), s_d, ids_d, lay.counts, num_tokens_per_rank=ntpr)
     y_expert = dsp.x_e * 2
     y = disp.combine(y_expert, lay.row_map, s_d, num_tokens_per_rank=ntpr)
-    torch.cuda.synchronize()
+    sync_or_fail()
     o = oracle.run_pipeline(x2, b["ids"], b["scores"], T, ntpr, w.E, w.K)
     assert np.array_equal(x_to_np(y), o["y"])
     del disp
@@ -403,6 +403,6 @@ def test_call_order_and_counts_are_enforced():
         disp.layout(ids_d, 65)
     disp.dispatch(x_d[:60], s_d[:60], ids_d[:60], lay.counts, num_tokens_per_rank=64)
     y = disp.combine(disp.x_e, lay.row_map, s_d[:60], num_tokens_per_rank=64)
-    torch.cuda.synchronize()
+    sync_or_fail()
     o = oracle.run_pipeline(b["x"], b["ids"], b["scores"], 60, 64, w.E, w.K)
     assert np.array_equal(x_to_np(y), o["y"])

@@ -12,7 +12,7 @@ import oracle
 import workloads
 from combine_moe_layout_05_amd import MoeDispatcher
 
-from gpu_util import DEV, ORACLE_THREADS, f32_dev, i32_dev, note, x_to_dev, x_to_np
+from gpu_util import DEV, ORACLE_THREADS, f32_dev, i32_dev, note, sync_or_fail, x_to_dev, x_to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def test_routing_map_conversion_parity(T, E, K, extra):
     disp = MoeDispatcher(T, 128, E, K, dtype=torch.bfloat16, device=DEV)
     note(f"routing map T={T} E={E} K={K}")
     gi, gs, gn = disp.topk_from_routing_map(torch.from_numpy(m.astype(bool)).to(DEV), f32_dev(p))
-    torch.cuda.synchronize()
+    sync_or_fail()
     oi, os_, on = oracle.topk_from_routing_map(m, p, K)
     np.testing.assert_array_equal(gi.cpu().numpy(), oi)
     assert np.array_equal(gs.cpu().numpy().view(np.uint32), os_.view(np.uint32))
@@ -71,7 +71,7 @@ def test_routing_map_end_to_end(name):
     lay = disp.layout(ids_d, w.ntpr)
     dsp = disp.dispatch(x_to_dev(b["x"][:T]), s_d, ids_d, lay.counts, num_tokens_per_rank=w.ntpr)
     y = disp.combine(dsp.x_e, lay.row_map, s_d, num_tokens_per_rank=w.ntpr)
-    torch.cuda.synchronize()
+    sync_or_fail()
     oi, os_, on = oracle.topk_from_routing_map(m, p, w.K)
     o = oracle.run_pipeline(b["x"], oi, os_, T, w.ntpr, w.E, w.K, nthreads=ORACLE_THREADS)
     np.testing.assert_array_equal(lay.counts.cpu().numpy(), o["counts"])
@@ -95,7 +95,7 @@ def test_scaled_dispatch_and_unit_combine(name, dtype):
     dsp = disp.dispatch_scaled(x_to_dev(b["x"][:T]), s_d, ids_d, lay.counts,
                                num_tokens_per_rank=w.ntpr)
     y = disp.combine(dsp.x_e, lay.row_map, None, num_tokens_per_rank=w.ntpr, T=T)
-    torch.cuda.synchronize()
+    sync_or_fail()
     total = int(lay.offsets[-1].item())
     lo = oracle.layout(b["ids"][:T], T, w.ntpr, w.E, w.K)
     xs = oracle.dispatch_scaled(b["x"][:T], b["scores"][:T], w.K, lo["src"], ORACLE_THREADS)
