@@ -14,7 +14,11 @@ default events is reported beside them).
 The line also carries, under "expert_step", the expert step between dispatch
 and combine (moe_grouped_gemm: one linear map per expert driven by the
 device-side offsets) at the workload's expert shape, timed over its own
-launches; it is not part of the step above.
+launches; it is not part of the step above. Under "configs" it carries the
+metric's other configurations timed the same way (tiny; the padded shape at
+T=3 and T=2047 of a 2048-token capacity; both 32k-token prefills; the graph
+shape at T=8192, eager and as a hipGraph replay), and under "cpu_baseline"
+the oracle on every host CPU the process may use ("host" gives the count).
 
     python bench.py [--steps K] [--warmup W] [--workload dsv3] [--expert-iters N]
 """
@@ -139,6 +143,11 @@ def parse_args():
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--expert-iters", type=int, default=10,
                    help="time the expert step (grouped GEMM) over this many launches; 0 skips")
+    p.add_argument("--configs", type=int, default=1,
+                   help="1: also time the other configurations of the metric (tiny, padded "
+                        "T=3 and 2047, both 32k prefills, the graph shape eager and replayed)")
+    p.add_argument("--config-steps", type=int, default=20,
+                   help="timed steps (and replays) per configuration")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run plain device write/read/copy of this size (HBM ceiling, "
                         "counter scaling)")
@@ -312,6 +321,175 @@ def time_expert_step(args, w, disp, ids, x, s, ntpr, dev) -> dict:
     }
 
 
+def load_batch(w, dev, T=None):
+    """Seeded synthetic batch of workload w on the device: (x, ids, scores,
+    host batch). With T, the first T rows of the workload's batch."""
+    import numpy as np
+    import torch
+
+    import workloads
+    b = workloads.make_batch(w)
+    if T is not None:
+        b = {k: v[:T] for k, v in b.items()}
+    if w.dtype == "bf16":
+        x = torch.from_numpy(np.ascontiguousarray(b["x"]).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(np.ascontiguousarray(b["x"])).to(dev)
+    ids = torch.from_numpy(np.ascontiguousarray(b["ids"])).to(dev)
+    s = torch.from_numpy(np.ascontiguousarray(b["scores"])).to(dev)
+    return x, ids, s, b
+
+
+def make_step(disp, x, ids, s, ntpr):
+    """One pass of the path: layout, dispatch, identity expert, combine. With
+    a list of 4 events, each call is bracketed by event records."""
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        lay = disp.layout(ids, ntpr)
+        if ev is not None:
+            ev[1].record()
+        disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
+        if ev is not None:
+            ev[2].record()
+        disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
+        if ev is not None:
+            ev[3].record()
+    return step
+
+
+def time_plain(step, steps: int) -> float:
+    """Milliseconds per step over `steps` back-to-back steps, no events."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_events(step, steps: int, make_event):
+    """Per-kernel milliseconds (layout, dispatch, combine lists) and the
+    wall milliseconds per step of a pass with events around each call."""
+    import torch
+    events = [[make_event() for _ in range(4)] for _ in range(steps)]
+    t_ev = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    per_step = (time.perf_counter() - t_ev) * 1e3 / steps
+    return ([e[0].elapsed_time(e[1]) for e in events],
+            [e[1].elapsed_time(e[2]) for e in events],
+            [e[2].elapsed_time(e[3]) for e in events], per_step)
+
+
+def time_graph(step, replays: int, dev) -> float:
+    """Microseconds per replay of one step captured into a hipGraph (warmed
+    up on a side stream first, as capture requires)."""
+    import torch
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    t_g = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t_g) * 1e6 / replays
+    del g
+    return us
+
+
+# The five configurations of the metric, each timed in the same run as the
+# headline: (key, workload, materialized T or None for the workload's T,
+# whether a graph replay is timed too, whether the roofline fraction means
+# anything at that size).
+CONFIGS = (
+    ("tiny", "tiny", None, False, False),
+    ("padded_T3", "padded", 3, False, False),
+    ("padded_T2047", "padded", 2047, False, True),
+    ("prefill32k_uniform", "prefill32k_uniform", None, False, True),
+    ("prefill32k_zipf", "prefill32k_zipf", None, False, True),
+    ("graph_T8192", "graph", None, True, True),
+)
+
+
+def measure_config(key, wname, T, graph, meaningful, steps, warmup, dev, make_event) -> dict:
+    """Tokens/s, per-kernel times and dispatch+combine GB/s (and fraction of
+    the HBM peak) of one configuration, timed like the headline."""
+    import gc
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from combine_moe_layout_05_amd import MoeDispatcher
+
+    w = workloads.WORKLOADS[wname]
+    T = w.T if T is None else T
+    log(f"config {key}: T={T} ntpr={w.ntpr} nmax={w.nmax} D={w.D} E={w.E} K={w.K} {w.dtype}")
+    x, ids, s, _ = load_batch(w, dev, T if T != w.T else None)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=dev)
+    step = make_step(disp, x, ids, s, w.ntpr)
+    for _ in range(warmup):
+        step()
+    ms = time_plain(step, steps)
+    lay_ms, dis_ms, com_ms, _ = time_events(step, steps, make_event)
+    kus = {"layout": float(np.mean(lay_ms)) * 1e3, "dispatch": float(np.mean(dis_ms)) * 1e3,
+           "combine": float(np.mean(com_ms)) * 1e3}
+    dc_us = kus["dispatch"] + kus["combine"]
+    dc_bytes = (bytes_per_token(w, "dispatch") + bytes_per_token(w, "combine")) * T
+    out = {"workload": wname, "T": T, "num_tokens_per_rank": w.ntpr,
+           "num_max_tokens_per_rank": w.nmax, "D": w.D, "E": w.E, "K": w.K, "dtype": w.dtype,
+           "routing": w.routing + (f"(s={w.zipf_s})" if w.routing == "zipf" else ""),
+           "steps": steps, "step_us": round(ms * 1e3, 2),
+           "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "kernels_us": {k: round(v, 2) for k, v in kus.items()},
+           "dispatch_combine_us": round(dc_us, 2),
+           "dispatch_combine_bytes": dc_bytes}
+    if meaningful:
+        gbps = dc_bytes / (dc_us * 1e-6) / 1e9
+        out["dispatch_combine_gbps"] = round(gbps, 1)
+        out["frac_of_peak"] = round(gbps / PEAK_HBM_GBPS, 4)
+    else:
+        out["note"] = "latency-bound size: microseconds only, no roofline fraction"
+    if graph:
+        g_us = time_graph(step, steps, dev)
+        out["graph_replay_us"] = round(g_us, 2)
+        out["graph_tokens_per_s"] = round(T / (g_us * 1e-6), 1)
+    log(f"config {key}: step {out['step_us']:.1f} us, dispatch+combine {dc_us:.1f} us"
+        + (f" ({out['frac_of_peak'] * 100:.1f} % of peak)" if meaningful else "")
+        + (f", graph replay {out['graph_replay_us']:.1f} us" if graph else ""))
+    del disp, x, ids, s, step
+    gc.collect()
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_cores() -> dict:
+    """Host CPUs this process may run on, with the cgroup CPU quota if one
+    is set (cgroup v2 cpu.max)."""
+    rec = {"affinity": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+           "cgroup_quota_cpus": None}
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            rec["cgroup_quota_cpus"] = round(int(quota) / int(period), 2)
+    except (OSError, ValueError):
+        pass
+    return rec
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -336,14 +514,8 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     w = workloads.WORKLOADS[args.workload]
     log(f"workload {w.name}: T={w.T} D={w.D} E={w.E} K={w.K} {w.dtype} {w.routing}")
-    b = workloads.make_batch(w)
+    x, ids, s, b = load_batch(w, dev)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    if w.dtype == "bf16":
-        x = torch.from_numpy(b["x"].view(np.int16)).to(dev).view(torch.bfloat16)
-    else:
-        x = torch.from_numpy(b["x"]).to(dev)
-    ids = torch.from_numpy(b["ids"]).to(dev)
-    s = torch.from_numpy(b["scores"]).to(dev)
     disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=dt, device=dev,
                          backward=args.backward > 0)
     disp.set_tuning(args.dispatch_segments, args.combine_segments,
@@ -354,19 +526,7 @@ def main() -> int:
                     else None, args.layout_launches, args.dispatch_store_burst)
     tuning = disp.get_tuning()
     ntpr = w.ntpr
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        lay = disp.layout(ids, ntpr)
-        if ev is not None:
-            ev[1].record()
-        disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr)
-        if ev is not None:
-            ev[2].record()
-        disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
-        if ev is not None:
-            ev[3].record()
+    step = make_step(disp, x, ids, s, ntpr)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -380,22 +540,10 @@ def main() -> int:
     # reported separately and does not set `value`).
     K = args.steps
     log(f"timed {K} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed = time_plain(step, K) * K * 1e-3
+
     def timed_pass(make_event):
-        events = [[make_event() for _ in range(4)] for _ in range(K)]
-        t_ev = time.perf_counter()
-        for i in range(K):
-            step(events[i])
-        torch.cuda.synchronize()
-        per_step = (time.perf_counter() - t_ev) * 1e3 / K
-        return ([e[0].elapsed_time(e[1]) for e in events],
-                [e[1].elapsed_time(e[2]) for e in events],
-                [e[2].elapsed_time(e[3]) for e in events], per_step)
+        return time_events(step, K, make_event)
 
     def torch_event():
         return torch.cuda.Event(enable_timing=True)
@@ -427,23 +575,7 @@ def main() -> int:
     graph_us = None
     if args.graph_replays > 0:
         log(f"graph capture of one step, {args.graph_replays} timed replays")
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream(dev).wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        g.replay()
-        torch.cuda.synchronize()
-        t_g = time.perf_counter()
-        for _ in range(args.graph_replays):
-            g.replay()
-        torch.cuda.synchronize()
-        graph_us = (time.perf_counter() - t_g) * 1e6 / args.graph_replays
-        del g
+        graph_us = time_graph(step, args.graph_replays, dev)
         log(f"graph replay {graph_us:.1f} us per step")
 
     # The same step with the layout fused into dispatch (moe_layout_dispatch:
@@ -573,9 +705,22 @@ def main() -> int:
         ref["dispatch_combine_over_copy"] = round(
             dc_bytes / (dc_ms * 1e-3) / 1e9 / ref["copy_gbps"], 4)
 
+    # The five configurations, each timed like the headline (the headline's
+    # own workload is the line's top level).
+    configs = None
+    if args.configs:
+        configs = {}
+        for key, wname, T, graph, meaningful in CONFIGS:
+            if wname == w.name and T is None:
+                continue
+            configs[key] = measure_config(key, wname, T, graph, meaningful, args.config_steps,
+                                          args.warmup, dev, main_event)
+
+    host = host_cores()
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = oracle_rate(max(1, min(16, len(os.sched_getaffinity(0)))), args.cpu_seconds)
+        # every host CPU this process may run on
+        cpu = oracle_rate(max(1, host["affinity"]), args.cpu_seconds)
     cpu_single = oracle_rate(1, args.cpu_single_seconds) if args.cpu_single_seconds > 0 else None
 
     def interval_stats(ms) -> dict:
@@ -622,6 +767,8 @@ def main() -> int:
         "fused_layout_dispatch": fused,
         "backward": backward,
         "expert_step": expert,
+        "configs": configs,
+        "host": host,
     }
     print(json.dumps(out), flush=True)
     return 0

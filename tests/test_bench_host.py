@@ -64,3 +64,22 @@ def test_more_than_one_gpu_is_refused():
                            env=dict(os.environ, **env))
         assert p.returncode == 2, p.stderr
         assert "one GPU only" in p.stderr and p.stdout == ""
+
+
+def test_configs_cover_the_five_configurations_of_the_metric():
+    """tiny; padded at T=3 and T=2047; both 32k prefills; the graph shape at
+    T=8192, eager and replayed (the DSV3 shape is the line's top level)."""
+    keys = [c[0] for c in bench.CONFIGS]
+    assert keys == ["tiny", "padded_T3", "padded_T2047", "prefill32k_uniform",
+                    "prefill32k_zipf", "graph_T8192"]
+    for key, wname, T, graph, meaningful in bench.CONFIGS:
+        w = workloads.WORKLOADS[wname]
+        assert T is None or 0 < T <= w.ntpr <= w.nmax
+        assert graph == (key == "graph_T8192")
+        assert meaningful == (key not in ("tiny", "padded_T3"))
+
+
+def test_host_cores_report_the_affinity():
+    rec = bench.host_cores()
+    assert rec["affinity"] == len(os.sched_getaffinity(0)) >= 1
+    assert rec["cgroup_quota_cpus"] is None or rec["cgroup_quota_cpus"] > 0
