@@ -8,8 +8,8 @@ ABI of include/moe.h); this package is its thin Python binding.
 """
 from .moe import (  # noqa: F401
     Dispatched, Layout, MoeDispatcher, TiledExpertWeights, ceil_div, grouped_gemm,
-    num_max_tokens_infer, num_max_tokens_pretrain, round_up4, tile_expert_weights,
-    validate_num_max,
+    layout_noalloc, num_max_tokens_infer, num_max_tokens_pretrain, round_up4,
+    tile_expert_weights, validate_num_max,
 )
 from ._lib import MoeError, load  # noqa: F401
 from .autograd import MoeTokenDispatcher  # noqa: F401

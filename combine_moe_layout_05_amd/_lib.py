@@ -20,6 +20,8 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_ERR_STATE = -5
 MOE_ERR_UNSUPPORTED = -6
+MOE_ERR_SCRATCH = -7
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 MOE_FLAG_BACKWARD = 1
 
@@ -62,6 +64,7 @@ SIGNATURES = {
     "moe_destroy": (_int, [_vp]),
     "moe_workspace_offsets": (_int, [_vp, C.POINTER(MoeBuffersDesc)]),
     "moe_layout": (_int, [_vp, _vp, _i32, _i32, _vp]),
+    "moe_layout_noalloc": (_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_dispatch": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "moe_combine": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, C.POINTER(_vp)]),
     "moe_dispatch_scaled": (_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 
 SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "combine_backward.hip", "routing_map.hip",
-           "grouped_gemm.hip",
+           "grouped_gemm.hip", "noalloc.hip",
            "moe_api.cpp"]
 HEADERS = [os.path.join(CSRC, "moe_kernels.h"), os.path.join(CSRC, "moe_lanes.h"),
            os.path.join(INCLUDE, "moe.h")]

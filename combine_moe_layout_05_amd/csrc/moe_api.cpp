@@ -189,6 +189,9 @@ const char* moe_strerror(int status) {
         case MOE_ERR_UNSUPPORTED:
             return "backward call on a context created without MOE_FLAG_BACKWARD, or fused "
                    "layout+dispatch on a context without a counter slot";
+        case MOE_ERR_SCRATCH:
+            return "moe_layout_noalloc needs more than its static scratch "
+                   "(MOE_NOALLOC_SCRATCH_BYTES); use moe_layout with a context";
         default: return "unknown status";
     }
 }
@@ -348,6 +351,35 @@ int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
     ctx->has_layout = true;
     ctx->layout_T = T;
     ctx->layout_ntpr4 = ntpr4;
+    return MOE_OK;
+}
+
+int moe_layout_noalloc(const int32_t* d_topk_ids, int32_t T, int32_t ntpr, int32_t E,
+                       int32_t K, int32_t* d_counts, int32_t* d_offsets, int32_t* d_row_map,
+                       int32_t* d_src_map, void* stream) {
+    if (E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || ntpr < T) return MOE_ERR_CAPACITY;
+    const int64_t nslots = moe_round_up4(ntpr) * K;
+    if (nslots > int64_t(INT32_MAX) - moe::kLayoutTile) return MOE_ERR_INVALID_ARG;
+    if (!d_counts || !d_offsets || !d_row_map || !d_src_map) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && !d_topk_ids) return MOE_ERR_INVALID_ARG;
+    static_assert(MOE_NOALLOC_SCRATCH_BYTES == moe::kNoallocScratchBytes, "one scratch size");
+    moe::LayoutArgs a;
+    a.ids = d_topk_ids;
+    a.nvalid = int64_t(T) * K;
+    a.nslots = nslots;
+    a.E = E;
+    a.counts = d_counts;
+    a.offsets = d_offsets;
+    a.row_map = d_row_map;
+    a.src_map = d_src_map;
+    a.launches = 0;
+    const int64_t need = moe::layout_hist_bytes(nslots, E, a.launches);
+    if (need > moe::kNoallocScratchBytes) return MOE_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (need > 0 && moe::noalloc_scratch(&scratch) != hipSuccess) return MOE_ERR_HIP;
+    a.block_hist = static_cast<int32_t*>(scratch);
+    if (moe::launch_layout(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -78,6 +78,14 @@ inline int64_t layout_hist_bytes(int64_t nslots, int32_t E, int32_t launches) {
     return layout_tiles(nslots, layout_slots_per_lane(nslots)) * padded_experts(E) * 4;
 }
 
+// Static scratch of moe_layout_noalloc, per device: the per-tile histograms
+// of the two-launch layout (4 MiB: e.g. 4096 tiles of 256 experts, 1024 of
+// 1024 experts).
+constexpr int64_t kNoallocScratchBytes = int64_t(4) << 20;
+// Device address of this device's scratch array (looked up once per device
+// with hipGetSymbolAddress; the device is the current one).
+hipError_t noalloc_scratch(void** out);
+
 // Bits needed to tell experts 0..E-1 apart (0 for E == 1).
 inline int expert_bits(int32_t E) {
     int b = 0;

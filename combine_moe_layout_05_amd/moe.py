@@ -138,6 +138,36 @@ def grouped_gemm(x_expert: torch.Tensor, weights, offsets: torch.Tensor,
     return out
 
 
+def layout_noalloc(topk_ids: torch.Tensor, num_experts: int, counts: torch.Tensor,
+                   offsets: torch.Tensor, row_map: torch.Tensor, src_map: torch.Tensor, *,
+                   num_tokens_per_rank: Optional[int] = None) -> None:
+    """moe_layout for callers that cannot allocate (moe_layout_noalloc): no
+    context, no workspace; the per-tile histograms live in the library's
+    static device scratch. Fills the caller's counts int32 [E], offsets
+    int32 [E+1], row_map int32 [round_up4(ntpr), K] and src_map int32
+    [>= T*K] (rows [0, total) written) from ids int32 [T, K], on the current
+    stream. Calls on one device must not overlap (they share the scratch)."""
+    dev = topk_ids.device
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, K]")
+    T, K = topk_ids.shape
+    ntpr = T if num_tokens_per_rank is None else int(num_tokens_per_rank)
+    n4 = round_up4(ntpr) if ntpr >= 0 else -1
+    want = (("topk_ids", topk_ids, None), ("counts", counts, (num_experts,)),
+            ("offsets", offsets, (num_experts + 1,)), ("row_map", row_map, (n4, K)),
+            ("src_map", src_map, None))
+    for name, t, shape in want:
+        if t.device != dev or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor on {dev}")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if src_map.numel() < T * K:
+        raise ValueError("src_map needs at least T * K entries")
+    L.check(L.load().moe_layout_noalloc(topk_ids.data_ptr(), T, ntpr, num_experts, K,
+                                        counts.data_ptr(), offsets.data_ptr(), row_map.data_ptr(),
+                                        src_map.data_ptr(), _stream(dev)), "moe_layout_noalloc")
+
+
 class MoeDispatcher:
     """One persistent workspace for MoE token layout, dispatch and combine.
 

@@ -59,6 +59,8 @@ extern "C" {
 #define MOE_ERR_STATE       (-5) /* dispatch/combine without a matching layout */
 #define MOE_ERR_UNSUPPORTED (-6) /* backward call without MOE_FLAG_BACKWARD; moe_layout_dispatch
                                     on a context that got no counter slot */
+#define MOE_ERR_SCRATCH     (-7) /* moe_layout_noalloc: the call needs more than the static
+                                    scratch (MOE_NOALLOC_SCRATCH_BYTES) */
 
 /* moe_config.flags */
 #define MOE_FLAG_BACKWARD   1    /* also carve the backward buffers g_e, g_s, g_x */
@@ -158,6 +160,37 @@ int moe_workspace_offsets(const moe_ctx *ctx, moe_buffers_desc *out);
  * host as the context's current layout. */
 int moe_layout(moe_ctx *ctx, const int32_t *d_topk_ids, int32_t T,
                int32_t num_tokens_per_rank, void *stream);
+
+/* moe_layout for callers that cannot allocate device memory: code running
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * No context and no workspace: the caller passes the ids and the four output
+ * buffers; the per-tile histograms the two-launch form needs live in a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES per device, which the
+ * library holds until the process ends. No device memory is allocated or
+ * freed. Results are those of moe_layout bit for bit:
+ *   d_topk_ids  int32 [T][K] (may be NULL when T == 0)
+ *   d_counts    int32 [num_experts]         written
+ *   d_offsets   int32 [num_experts + 1]     written; d_offsets[E] = total
+ *   d_row_map   int32 [round_up4(num_tokens_per_rank)][K]  written
+ *   d_src_map   int32 [>= total] (at most T*K); rows [0, total) written
+ * Requires 0 <= T <= num_tokens_per_rank (MOE_ERR_CAPACITY), 1 <= num_experts
+ * <= MOE_MAX_EXPERTS, 1 <= topk <= MOE_MAX_TOPK and
+ * round_up4(num_tokens_per_rank) * topk < 2^31 - 512 (MOE_ERR_INVALID_ARG).
+ * Scratch limit: up to 32768 slots (round_up4(num_tokens_per_rank) * topk)
+ * the layout is one launch and uses no scratch; above, it uses
+ * ceil(slots / tile) * round_up4(num_experts) * 4 bytes (tile = 512 slots up
+ * to 65536 slots, 1024 above), and a call needing more than
+ * MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH (e.g. beyond 4194304
+ * slots at 256 experts, 1048576 at 1024). Every call on one device shares
+ * that device's array, so calls that overlap on one device race: order them
+ * on one stream. The first call on each device that needs the scratch looks
+ * up its device address (a host-side query, done once); make that call
+ * outside graph capture. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4 << 20)
+int moe_layout_noalloc(const int32_t *d_topk_ids, int32_t T, int32_t num_tokens_per_rank,
+                       int32_t num_experts, int32_t topk, int32_t *d_counts,
+                       int32_t *d_offsets, int32_t *d_row_map, int32_t *d_src_map,
+                       void *stream);
 
 /* Dispatch ([TT] "API design" signature; [NA] "Fix"). Permutes the hidden
  * states into the context's expert-major buffer using the row map of the

@@ -152,8 +152,28 @@ int main() {
     EXPECT(moe_num_max_tokens_infer(32768, 1, 1) == 32768);
     EXPECT(moe_validate_num_max(100, 99) == MOE_OK && moe_validate_num_max(0, 0) != MOE_OK);
     EXPECT(moe_check_capacity(3, 4, 8) == MOE_OK && moe_check_capacity(5, 4, 8) != MOE_OK);
-    for (int s = -7; s <= 0; ++s) EXPECT(moe_strerror(s) != nullptr);
+    for (int s = -8; s <= 0; ++s) EXPECT(moe_strerror(s) != nullptr);
 
+    // layout without a context (static scratch above 32768 slots)
+    {
+        void* q = fake(uintptr_t(1) << 41);
+        const int32_t* ids = static_cast<const int32_t*>(q);
+        int32_t* o = static_cast<int32_t*>(q);
+        const int32_t sizes[][4] = {  // T, ntpr, E, K
+            {0, 0, 8, 2}, {61, 64, 8, 2}, {4096, 4096, 256, 8}, {8191, 8192, 128, 8},
+            {32768, 32768, 256, 8}, {131072, 131072, 1024, 8}, {0, 524288, 256, 8},
+        };
+        for (const auto& c : sizes)
+            EXPECT(moe_layout_noalloc(c[0] ? ids : nullptr, c[0], c[1], c[2], c[3], o, o, o, o,
+                                      nullptr) == MOE_OK);
+        EXPECT(moe_layout_noalloc(ids, 0, 131076, 1024, 8, o, o, o, o, nullptr) == MOE_ERR_SCRATCH);
+        EXPECT(moe_layout_noalloc(ids, 0, 524292, 256, 8, o, o, o, o, nullptr) == MOE_ERR_SCRATCH);
+        EXPECT(moe_layout_noalloc(ids, 9, 8, 8, 2, o, o, o, o, nullptr) == MOE_ERR_CAPACITY);
+        EXPECT(moe_layout_noalloc(ids, 8, 8, 8, 2, o, o, nullptr, o, nullptr) ==
+               MOE_ERR_INVALID_ARG);
+        EXPECT(moe_layout_noalloc(nullptr, 8, 8, 8, 2, o, o, o, o, nullptr) == MOE_ERR_INVALID_ARG);
+        EXPECT(moe_layout_noalloc(ids, 8, 8, 0, 2, o, o, o, o, nullptr) == MOE_ERR_INVALID_ARG);
+    }
 
     // expert step
     void* p = fake(uintptr_t(1) << 41);

@@ -340,3 +340,29 @@ def test_product_path_does_not_import_the_oracle():
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "moe_oracle" not in text and "liborc" not in text, f
 
+
+def test_layout_noalloc_rejects_bad_arguments_before_any_launch(lib):
+    """moe_layout_noalloc checks everything on the host first, so these calls
+    return without touching a device (the pointers are never dereferenced):
+    sizes, the capacity relation, null pointers, and inputs whose per-tile
+    histograms would not fit the static scratch."""
+    p = C.c_void_p(1 << 40)
+    f = lib.moe_layout_noalloc
+    assert f(p, 5, 8, 0, 8, p, p, p, p, None) == L.MOE_ERR_INVALID_ARG        # E = 0
+    assert f(p, 5, 8, 1025, 8, p, p, p, p, None) == L.MOE_ERR_INVALID_ARG     # E > max
+    assert f(p, 5, 8, 16, 17, p, p, p, p, None) == L.MOE_ERR_INVALID_ARG      # K > max
+    assert f(p, 9, 8, 16, 2, p, p, p, p, None) == L.MOE_ERR_CAPACITY          # T > ntpr
+    assert f(p, -1, 8, 16, 2, p, p, p, p, None) == L.MOE_ERR_CAPACITY
+    assert f(None, 5, 8, 16, 2, p, p, p, p, None) == L.MOE_ERR_INVALID_ARG    # ids, T > 0
+    for i in range(4):
+        outs = [p, p, p, p]
+        outs[i] = None
+        assert f(p, 5, 8, 16, 2, *outs, None) == L.MOE_ERR_INVALID_ARG
+    assert f(p, 0, (2**31 - 512) // 16 + 4, 16, 16, p, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    # Scratch: 1024-slot tiles above 65536 slots, one row of round_up4(E)
+    # int32 per tile, 4 MiB in all.
+    assert L.MOE_NOALLOC_SCRATCH_BYTES == 4 << 20
+    assert f(p, 0, 131076, 1024, 8, p, p, p, p, None) == L.MOE_ERR_SCRATCH    # 1025 tiles x 4 KiB
+    assert f(p, 0, 524292, 256, 8, p, p, p, p, None) == L.MOE_ERR_SCRATCH     # 4097 tiles x 1 KiB
+    assert f(p, 131076, 131076, 1024, 8, p, p, p, p, None) == L.MOE_ERR_SCRATCH
+    assert b"static scratch" in lib.moe_strerror(L.MOE_ERR_SCRATCH)
