@@ -143,6 +143,8 @@ def parse_args():
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--expert-iters", type=int, default=10,
                    help="time the expert step (grouped GEMM) over this many launches; 0 skips")
+    p.add_argument("--ceiling-iters", type=int, default=20,
+                   help="time the combine beside its no-arithmetic traffic probes (0 = skip)")
     p.add_argument("--configs", type=int, default=1,
                    help="1: also time the other configurations of the metric (tiny, padded "
                         "T=3 and 2047, both 32k prefills, the graph shape eager and replayed)")
@@ -475,6 +477,87 @@ def measure_config(key, wname, T, graph, meaningful, steps, warmup, dev, make_ev
     return out
 
 
+def combine_ceiling(disp, x, ids, s, w, dev, make_event, iters: int) -> dict:
+    """The combine beside kernels that move its exact HBM traffic with no
+    arithmetic (libmoe_traffic_probe.so): the gather-copy (same reads, same
+    launch shape, the XOR of the K rows stored), the same reads with no
+    store, the same read:write byte ratio in sequential order, and a plain
+    sequential read of the same bytes. Each is
+    timed by fence-free events both right after layout + dispatch (the
+    step's context: dispatch's writes are still draining) and after a 1 GiB
+    read has evicted the caches ("cold")."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from combine_moe_layout_05_amd._paths import PROBE_LIB_PATH
+
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise RuntimeError(f"{PROBE_LIB_PATH} is not built")
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.probe_gather_copy.argtypes = [vp, vp, i32, i32, i32, i64, vp, vp, ctypes.c_int, vp]
+    lib.probe_stream.argtypes = [ctypes.c_int, vp, vp, i64, vp, vp]
+    ntpr = w.ntpr
+    rows = (w.ntpr + 3) // 4 * 4 * w.K
+    chunks = w.D * (2 if w.dtype == "bf16" else 4) // 16
+    out = torch.empty((w.T, w.D), dtype=disp.dtype, device=dev)
+    sink = torch.full((4,), 0x7FC17FC1, dtype=torch.int32, device=dev)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sinkf = torch.empty((), dtype=torch.float32, device=dev)
+    stream = lambda: torch.cuda.current_stream(dev).cuda_stream  # noqa: E731
+    lay = disp.layout(ids, ntpr)
+
+    def gather(store):
+        rc = lib.probe_gather_copy(disp.x_e.data_ptr(), lay.row_map.data_ptr(), w.T, w.K, chunks,
+                                   rows, out.data_ptr(), sink.data_ptr(), store, stream())
+        if rc != 0:
+            raise RuntimeError(f"probe_gather_copy failed ({rc})")
+
+    read_bytes = w.T * w.K * chunks * 16
+
+    def streaming(kind):
+        rc = lib.probe_stream(kind, disp.x_e.data_ptr(), out.data_ptr(), read_bytes,
+                              sink.data_ptr(), stream())
+        if rc != 0:
+            raise RuntimeError(f"probe_stream failed ({rc})")
+
+    kernels = {
+        "combine": lambda: disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr),
+        "gather_copy": lambda: gather(1),
+        "gather_read": lambda: gather(0),
+        "sequential_mix": lambda: streaming(2),
+        "sequential_read": lambda: streaming(0),
+    }
+    res = {}
+    for name, fn in kernels.items():
+        for where in ("step", "cold"):
+            us = []
+            for i in range(iters + 2):
+                if where == "step":
+                    lay2 = disp.layout(ids, ntpr)
+                    disp.dispatch(x, s, ids, lay2.counts, num_tokens_per_rank=ntpr)
+                else:
+                    torch.sum(scratch, dim=0, out=sinkf)
+                e0, e1 = make_event(), make_event()
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                if i >= 2:
+                    us.append(e0.elapsed_time(e1) * 1e3)
+            res[f"{name}_{where}_us"] = round(float(np.median(us)), 2)
+    res["combine_over_gather_copy_step"] = round(res["combine_step_us"] / res["gather_copy_step_us"], 4)
+    res["combine_over_gather_copy_cold"] = round(res["combine_cold_us"] / res["gather_copy_cold_us"], 4)
+    res["bytes"] = {"combine_and_gather_copy": bytes_per_token(w, "combine") * w.T,
+                    "gather_read": read_bytes, "sequential_mix": read_bytes + read_bytes // 8,
+                    "sequential_read": read_bytes}
+    del out, scratch
+    torch.cuda.empty_cache()
+    return res
+
+
 def host_cores() -> dict:
     """Host CPUs this process may run on, with the cgroup CPU quota if one
     is set (cgroup v2 cpu.max)."""
@@ -664,6 +747,14 @@ def main() -> int:
                                                     / (db * 1e-6) / 1e9, 1)}
         log(f"backward: combine_backward {cb:.1f} us, dispatch_backward {db:.1f} us")
 
+    ceiling = None
+    if args.ceiling_iters > 0:
+        log(f"combine beside its traffic probes, {args.ceiling_iters} iterations each")
+        ceiling = combine_ceiling(disp, x, ids, s, w, dev, main_event, args.ceiling_iters)
+        log(f"combine {ceiling['combine_step_us']:.1f} us against the gather-copy "
+            f"{ceiling['gather_copy_step_us']:.1f} us in the step, "
+            f"{ceiling['combine_cold_us']:.1f} / {ceiling['gather_copy_cold_us']:.1f} us cold")
+
     expert = None
     if args.expert_iters > 0 and w.name in workloads.EXPERT_SHAPES:
         expert = time_expert_step(args, w, disp, ids, x, s, ntpr, dev)
@@ -767,6 +858,7 @@ def main() -> int:
         "fused_layout_dispatch": fused,
         "backward": backward,
         "expert_step": expert,
+        "combine_ceiling": ceiling,
         "configs": configs,
         "host": host,
     }

@@ -10,10 +10,10 @@ import subprocess
 import sys
 
 if __package__:
-    from ._paths import LIB_PATH, PKG
+    from ._paths import LIB_PATH, PKG, PROBE_LIB_PATH
 else:  # run as a script
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    from _paths import LIB_PATH, PKG  # type: ignore
+    from _paths import LIB_PATH, PKG, PROBE_LIB_PATH  # type: ignore
 
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
@@ -24,6 +24,8 @@ SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "combine_backward.hip", 
            "moe_api.cpp"]
 HEADERS = [os.path.join(CSRC, "moe_kernels.h"), os.path.join(CSRC, "moe_lanes.h"),
            os.path.join(INCLUDE, "moe.h")]
+# The benchmark's traffic reference kernels, built into a library of their own.
+PROBE_SOURCES = ["traffic_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -51,13 +53,20 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every source into combine_moe_layout_05_amd/libmoe_layout.so
-    (one hipcc process per source file in parallel, then one link)."""
+    (one hipcc process per source file in parallel, then one link), and the
+    benchmark's traffic reference kernels into libmoe_traffic_probe.so."""
+    lib = _build_library(SOURCES, LIB_PATH, verbose)
+    _build_library(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
+    return lib
+
+
+def _build_library(sources, out_path: str, verbose: bool) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
         cmd = [hipcc(), *compile_flags, "-I", INCLUDE, "-I", CSRC, "-c",
@@ -74,7 +83,7 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(out)
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    tmp = out_path + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -82,16 +91,18 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc link failed with status {res.returncode}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB_PATH):
-        return True
-    t = os.path.getmtime(LIB_PATH)
-    return any(os.path.getmtime(p) > t for p in
-               [os.path.join(CSRC, s) for s in SOURCES] + HEADERS)
+    for lib, sources in ((LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)):
+        if not os.path.exists(lib):
+            return True
+        t = os.path.getmtime(lib)
+        if any(os.path.getmtime(p) > t for p in [os.path.join(CSRC, s) for s in sources] + HEADERS):
+            return True
+    return False
 
 
 if __name__ == "__main__":

@@ -83,3 +83,16 @@ def test_host_cores_report_the_affinity():
     rec = bench.host_cores()
     assert rec["affinity"] == len(os.sched_getaffinity(0)) >= 1
     assert rec["cgroup_quota_cpus"] is None or rec["cgroup_quota_cpus"] > 0
+
+
+def test_traffic_probe_library_is_built_apart_from_the_product():
+    """bench.py's traffic reference kernels live in their own library; the
+    product library exports none of them."""
+    import ctypes
+
+    from combine_moe_layout_05_amd import _lib
+    from combine_moe_layout_05_amd._paths import PROBE_LIB_PATH
+    probe = ctypes.CDLL(PROBE_LIB_PATH)
+    assert hasattr(probe, "probe_gather_copy") and hasattr(probe, "probe_stream")
+    product = _lib.load()
+    assert not hasattr(product, "probe_gather_copy")
