@@ -35,7 +35,9 @@ class _Dispatch(torch.autograd.Function):
         total = lay.offsets[-1:].clone()
         ctx.disp, ctx.T, ctx.ntpr, ctx.row_map = disp, x.shape[0], ntpr, row_map
         ctx.mark_non_differentiable(row_map, total)
-        x_e = out.x_e.clone() if clone_x_e else out.x_e
+        # A fresh tensor object per call: autograd attaches this call's node to
+        # it, and the binding hands out one shared view per extent.
+        x_e = out.x_e.clone() if clone_x_e else out.x_e.view(out.x_e.shape)
         return x_e, row_map, total
 
     @staticmethod

@@ -36,7 +36,15 @@ class Dispatched(NamedTuple):
     s_e: torch.Tensor        # float32 [round_up4(ntpr) * K]; rows [0, total) valid
 
 
+# torch's current HIP stream of a device as a raw handle. The private getter
+# returns the handle without building a Python stream object (about 0.1 us
+# against 2 us per call); the public API serves when it is absent.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -44,8 +52,19 @@ def ceil_div(a: int, b: int) -> int:
     return int(L.load().moe_ceil_div(a, b))
 
 
+_round_up4_cache: dict = {}
+
+
 def round_up4(n: int) -> int:
-    return int(L.load().moe_round_up4(n))
+    """moe_round_up4 of the library, remembered per argument (the calls take
+    a capacity that rarely changes, and a ctypes call per use costs more than
+    the launch it sizes)."""
+    r = _round_up4_cache.get(n)
+    if r is None:
+        r = int(L.load().moe_round_up4(n))
+        if len(_round_up4_cache) < 4096:
+            _round_up4_cache[n] = r
+    return r
 
 
 def num_max_tokens_pretrain(local_batch: int, seq_len: int, cp: int = 1, tp: int = 1) -> int:
@@ -175,6 +194,11 @@ class MoeDispatcher:
     lifetime maximum, and carved by the library into fixed-address buffers;
     no later call allocates, grows, synchronizes or reads back.
 
+    The views the calls return (Layout, Dispatched, combine's y[:T]) are
+    made once per extent and shared by every call with that extent: they
+    always show the buffers' current contents, and their metadata (shape,
+    requires_grad) should not be changed; take a view or a copy for that.
+
     x_e_generation counts the calls that rewrote x_e (dispatch,
     dispatch_scaled, layout_dispatch), so a holder of an x_e view can tell
     whether the rows it saw are still there. close() (also run when the
@@ -199,6 +223,10 @@ class MoeDispatcher:
         self.num_max_tokens_per_rank = num_max_tokens_per_rank
         self.backward_enabled = bool(backward)
         self.x_e_generation = 0
+        self._dev_index = self.device.index
+        self._views: dict = {}
+        self._out = C.c_void_p()
+        self._out_ref = C.byref(self._out)
         self._cfg = L.MoeConfig(num_max_tokens_per_rank, hidden, num_experts, topk,
                                 _DTYPES[dtype], L.MOE_FLAG_BACKWARD if backward else 0)
         nbytes = C.c_size_t(0)
@@ -260,15 +288,24 @@ class MoeDispatcher:
 
     # -- argument checks (marshalling) -------------------------------------
     def _dev(self, t: torch.Tensor, name: str, dtype: torch.dtype, cols: int) -> torch.Tensor:
-        if t.device != self.device:
-            raise ValueError(f"{name} must be on {self.device}, got {t.device}")
         if t.dtype != dtype:
             raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_cuda or t.get_device() != self._dev_index:
+            raise ValueError(f"{name} must be on {self.device}, got {t.device}")
         if t.dim() != 2 or t.shape[1] != cols:
             raise ValueError(f"{name} must be [T, {cols}], got {tuple(t.shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         return t
+
+    def _cached(self, key, make):
+        """A view of a persistent buffer, made once per (buffer, extent)."""
+        v = self._views.get(key)
+        if v is None:
+            v = make()
+            if len(self._views) < 1024:
+                self._views[key] = v
+        return v
 
     def _ntpr(self, T: int, num_tokens_per_rank: Optional[int]) -> int:
         return T if num_tokens_per_rank is None else int(num_tokens_per_rank)
@@ -282,7 +319,8 @@ class MoeDispatcher:
         L.check(self._lib.moe_layout(self._ctx, ids.data_ptr(), T, ntpr, _stream(self.device)),
                 "moe_layout")
         n4 = round_up4(ntpr)
-        return Layout(self.counts, self.offsets, self.row_map[:n4])
+        return self._cached(("layout", n4),
+                            lambda: Layout(self.counts, self.offsets, self.row_map[:n4]))
 
     def dispatch(self, x_TD: torch.Tensor, topk_scores_TK: torch.Tensor,
                  topk_expert_ids_TK: torch.Tensor, num_local_tokens_per_expert_E: torch.Tensor,
@@ -316,7 +354,8 @@ class MoeDispatcher:
                    ntpr, _stream(self.device)), what)
         self.x_e_generation += 1
         rows = round_up4(ntpr) * self.topk
-        return Dispatched(self.x_e[:rows], self.s_e[:rows])
+        return self._cached(("dispatched", rows),
+                            lambda: Dispatched(self.x_e[:rows], self.s_e[:rows]))
 
     def layout_dispatch(self, x_TD: torch.Tensor, topk_scores_TK: torch.Tensor,
                         topk_expert_ids_TK: torch.Tensor, *,
@@ -375,7 +414,8 @@ class MoeDispatcher:
                 raise ValueError("T differs from topk_scores_TK.shape[0]")
             T = s.shape[0]
             s_ptr = s.data_ptr()
-        if y_expert.device != self.device or y_expert.dtype != self.dtype:
+        if (y_expert.dtype != self.dtype or not y_expert.is_cuda
+                or y_expert.get_device() != self._dev_index):
             raise TypeError("y_expert must match the dispatcher's device and dtype")
         if y_expert.dim() != 2 or y_expert.shape[1] != self.hidden or not y_expert.is_contiguous():
             raise ValueError(f"y_expert must be a contiguous [rows, {self.hidden}] tensor")
@@ -383,11 +423,10 @@ class MoeDispatcher:
         ntpr = self._ntpr(T, num_tokens_per_rank)
         if y_expert.shape[0] < round_up4(ntpr) * self.topk:
             raise ValueError("y_expert needs round_up4(num_tokens_per_rank) * topk rows")
-        out = C.c_void_p()
         L.check(self._lib.moe_combine(self._ctx, y_expert.data_ptr(), rm.data_ptr(), s_ptr,
-                                      T, ntpr, _stream(self.device), C.byref(out)),
+                                      T, ntpr, _stream(self.device), self._out_ref),
                 "moe_combine")
-        return self.y[:T]
+        return self._cached(("y", T), lambda: self.y[:T])
 
     # -- backward ----------------------------------------------------------
     def _expert_rows(self, t: torch.Tensor, name: str, ntpr: int) -> torch.Tensor:
@@ -400,7 +439,8 @@ class MoeDispatcher:
         return t
 
     def _row_map(self, rm: torch.Tensor, T: int) -> torch.Tensor:
-        if rm.device != self.device or rm.dtype != torch.int32 or not rm.is_contiguous():
+        if (rm.dtype != torch.int32 or not rm.is_cuda or rm.get_device() != self._dev_index
+                or not rm.is_contiguous()):
             raise ValueError("row_map must be a contiguous int32 tensor on the device")
         if rm.dim() != 2 or rm.shape[1] != self.topk or rm.shape[0] < T:
             raise ValueError(f"row_map must be [>= T, {self.topk}]")
