@@ -117,8 +117,9 @@ def parse_args():
     p.add_argument("--events", choices=["fence_free", "system"], default="fence_free",
                    help="per-kernel timing events: created with hipEventDisableSystemFence "
                         "(default) or torch's default events (system-scope fence at each record)")
-    p.add_argument("--fused-steps", type=int, default=50,
-                   help="also time the step with moe_layout_dispatch (0 = skip)")
+    p.add_argument("--fused-steps", type=int, default=0,
+                   help="also time the step with moe_layout_dispatch (0 = skip, the default: "
+                        "it does not beat the separate calls on MI355X)")
     p.add_argument("--copy-reference", type=int, default=1,
                    help="1: also time a plain 1 GiB device write and copy (0 = skip)")
     p.add_argument("--cpu-single-seconds", type=float, default=3.0,
@@ -386,9 +387,11 @@ def time_events(step, steps: int, make_event):
             [e[2].elapsed_time(e[3]) for e in events], per_step)
 
 
-def time_graph(step, replays: int, dev) -> float:
-    """Microseconds per replay of one step captured into a hipGraph (warmed
-    up on a side stream first, as capture requires)."""
+def time_graph(step, replays: int, dev, steps_per_graph: int = 1) -> float:
+    """Microseconds per step of a hipGraph holding `steps_per_graph` steps,
+    over `replays` replays (warmed up on a side stream first, as capture
+    requires). Each graph launch costs a fixed few microseconds on the host
+    and the GPU, which a graph holding more work pays once."""
     import torch
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
@@ -398,14 +401,15 @@ def time_graph(step, replays: int, dev) -> float:
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        step()
+        for _ in range(steps_per_graph):
+            step()
     g.replay()
     torch.cuda.synchronize()
     t_g = time.perf_counter()
     for _ in range(replays):
         g.replay()
     torch.cuda.synchronize()
-    us = (time.perf_counter() - t_g) * 1e6 / replays
+    us = (time.perf_counter() - t_g) * 1e6 / (replays * steps_per_graph)
     del g
     return us
 
@@ -468,6 +472,10 @@ def measure_config(key, wname, T, graph, meaningful, steps, warmup, dev, make_ev
         g_us = time_graph(step, steps, dev)
         out["graph_replay_us"] = round(g_us, 2)
         out["graph_tokens_per_s"] = round(T / (g_us * 1e-6), 1)
+    # Ten steps per graph: the per-launch cost amortized, as in a captured
+    # layer; at the small shapes this is the GPU-side step latency.
+    g10 = time_graph(step, max(2, steps // 5), dev, steps_per_graph=10)
+    out["graph_10_steps_us_per_step"] = round(g10, 2)
     log(f"config {key}: step {out['step_us']:.1f} us, dispatch+combine {dc_us:.1f} us"
         + (f" ({out['frac_of_peak'] * 100:.1f} % of peak)" if meaningful else "")
         + (f", graph replay {out['graph_replay_us']:.1f} us" if graph else ""))
@@ -655,11 +663,12 @@ def main() -> int:
 
     # The same step captured once into a hipGraph and replayed: the launch
     # gaps between the kernels disappear.
-    graph_us = None
+    graph_us = graph10_us = None
     if args.graph_replays > 0:
         log(f"graph capture of one step, {args.graph_replays} timed replays")
         graph_us = time_graph(step, args.graph_replays, dev)
-        log(f"graph replay {graph_us:.1f} us per step")
+        graph10_us = time_graph(step, max(2, args.graph_replays // 5), dev, steps_per_graph=10)
+        log(f"graph replay {graph_us:.1f} us per step; ten steps per graph {graph10_us:.1f} us per step")
 
     # The same step with the layout fused into dispatch (moe_layout_dispatch:
     # two launches instead of three), timed the same way; reported beside the
@@ -852,6 +861,7 @@ def main() -> int:
         "cold_cache": cold,
         "device_copy_reference": ref,
         "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
+        "graph_10_steps_us_per_step": None if graph10_us is None else round(graph10_us, 2),
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "kernel_events": args.events,
         "kernels_with_other_events": other_events,
