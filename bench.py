@@ -490,7 +490,8 @@ def combine_ceiling(disp, x, ids, s, w, dev, make_event, iters: int) -> dict:
     arithmetic (libmoe_traffic_probe.so): the gather-copy (same reads, same
     launch shape, the XOR of the K rows stored), the same reads with no
     store, the same read:write byte ratio in sequential order, and a plain
-    sequential read of the same bytes. Each is
+    sequential read of the same bytes; and dispatch beside a sequential
+    stream of its own byte ratio (1 read : 8 written). Each is
     timed by fence-free events both right after layout + dispatch (the
     step's context: dispatch's writes are still draining) and after a 1 GiB
     read has evicted the caches ("cold")."""
@@ -556,11 +557,47 @@ def combine_ceiling(disp, x, ids, s, w, dev, make_event, iters: int) -> dict:
                 if i >= 2:
                     us.append(e0.elapsed_time(e1) * 1e3)
             res[f"{name}_{where}_us"] = round(float(np.median(us)), 2)
+    # Dispatch beside the same bytes in sequential order (one 1 KiB read
+    # written to eight consecutive KiB): in a step it follows the previous
+    # step's combine and this step's layout.
+    x_bytes = w.T * chunks * 16
+
+    def seq_1to8():
+        rc = lib.probe_stream(3, x.data_ptr(), disp.x_e.data_ptr(), x_bytes, sink.data_ptr(),
+                              stream())
+        if rc != 0:
+            raise RuntimeError(f"probe_stream failed ({rc})")
+
+    dkernels = {"dispatch": lambda: disp.dispatch(x, s, ids, lay.counts, num_tokens_per_rank=ntpr),
+                "sequential_1to8": seq_1to8}
+    for name, fn in dkernels.items():
+        for where in ("step", "cold"):
+            us = []
+            for i in range(iters + 2):
+                if where == "step":
+                    disp.combine(disp.x_e, lay.row_map, s, num_tokens_per_rank=ntpr)
+                    disp.layout(ids, ntpr)
+                else:
+                    disp.layout(ids, ntpr)
+                    torch.sum(scratch, dim=0, out=sinkf)
+                e0, e1 = make_event(), make_event()
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                if i >= 2:
+                    us.append(e0.elapsed_time(e1) * 1e3)
+            res[f"{name}_{where}_us"] = round(float(np.median(us)), 2)
     res["combine_over_gather_copy_step"] = round(res["combine_step_us"] / res["gather_copy_step_us"], 4)
     res["combine_over_gather_copy_cold"] = round(res["combine_cold_us"] / res["gather_copy_cold_us"], 4)
+    res["dispatch_over_sequential_1to8_step"] = round(
+        res["dispatch_step_us"] / res["sequential_1to8_step_us"], 4)
+    res["dispatch_over_sequential_1to8_cold"] = round(
+        res["dispatch_cold_us"] / res["sequential_1to8_cold_us"], 4)
     res["bytes"] = {"combine_and_gather_copy": bytes_per_token(w, "combine") * w.T,
                     "gather_read": read_bytes, "sequential_mix": read_bytes + read_bytes // 8,
-                    "sequential_read": read_bytes}
+                    "sequential_read": read_bytes, "dispatch": bytes_per_token(w, "dispatch") * w.T,
+                    "sequential_1to8": 9 * x_bytes}
     del out, scratch
     torch.cuda.empty_cache()
     return res

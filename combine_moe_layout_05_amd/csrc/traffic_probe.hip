@@ -13,7 +13,10 @@
 //                      (eight 1 KiB pieces per wavefront), 1 = write
 //                      (1 KiB per wavefront), 2 = the combine's read:write
 //                      byte ratio in sequential order (eight consecutive
-//                      1 KiB reads, one 1 KiB write into a second buffer)
+//                      1 KiB reads, one 1 KiB write into a second buffer),
+//                      3 = dispatch's read:write byte ratio in sequential
+//                      order (one 1 KiB read, written to eight consecutive
+//                      KiB of a second buffer)
 //
 // Reads are kept alive by comparing the loaded data with three words of
 // `sink` that the caller sets to values the data never takes; a kernel that
@@ -80,8 +83,8 @@ void gather_copy_kernel(const v4i* __restrict__ rows, const int32_t* __restrict_
     }
 }
 
-// kind 0: read; 1: write; 2: sequential 8:1 read:write mix. One kernel per
-// kind, so traces and counters name them apart.
+// kind 0: read; 1: write; 2: sequential 8:1 read:write mix; 3: sequential
+// 1:8 mix. One kernel per kind, so traces and counters name them apart.
 template <int KIND>
 __global__ __launch_bounds__(1024)
 void stream_kernel(const v4i* __restrict__ a, v4i* __restrict__ b, int64_t n_chunks,
@@ -91,6 +94,15 @@ void stream_kernel(const v4i* __restrict__ a, v4i* __restrict__ b, int64_t n_chu
     if constexpr (KIND == 1) {
         const int64_t c = w * 64 + lane;
         if (c < n_chunks) b[c] = v4i{static_cast<int32_t>(c), 1, 2, 3};
+        return;
+    }
+    if constexpr (KIND == 3) {
+        const int64_t c = w * 64 + lane;
+        if (c < n_chunks) {
+            const v4i v = a[c];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) b[(w * 8 + i) * 64 + lane] = v;
+        }
         return;
     }
     v4i acc = {0, 0, 0, 0};
@@ -146,15 +158,19 @@ int probe_gather_copy(const void* rows, const int32_t* row_map, int32_t T, int32
 }
 
 // kind 0: read `bytes` of a; 1: write `bytes` of b; 2: read `bytes` of a and
-// write bytes / 8 of b (sequential). bytes: a multiple of 16 (of 128 for 2).
+// write bytes / 8 of b (sequential); 3: read `bytes` of a and write 8 x bytes
+// of b (sequential). bytes: a multiple of 16 (of 128 for 2, of 1024 for 3).
 int probe_stream(int kind, const void* a, void* b, int64_t bytes, int32_t* sink, void* stream) {
-    if (kind < 0 || kind > 2 || bytes <= 0 || bytes % (kind == 2 ? 128 : 16) != 0 || !sink)
+    const int64_t unit = kind == 2 ? 128 : (kind == 3 ? 1024 : 16);
+    if (kind < 0 || kind > 3 || bytes <= 0 || bytes % unit != 0 || !sink)
         return hipErrorInvalidValue;
     if ((kind != 1 && !a) || (kind != 0 && !b)) return hipErrorInvalidValue;
     const int64_t n = bytes / 16;
-    const int64_t waves = kind == 1 ? (n + 63) / 64 : (n + 511) / 512;
+    const int64_t waves = (kind == 1 || kind == 3) ? (n + 63) / 64 : (n + 511) / 512;
     const int64_t blocks = (waves + 15) / 16;
-    auto kernel = kind == 0 ? stream_kernel<0> : kind == 1 ? stream_kernel<1> : stream_kernel<2>;
+    auto kernel = kind == 0 ? stream_kernel<0>
+                : kind == 1 ? stream_kernel<1>
+                : kind == 2 ? stream_kernel<2> : stream_kernel<3>;
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0,
                        static_cast<hipStream_t>(stream), static_cast<const v4i*>(a),
                        static_cast<v4i*>(b), n, sink);

@@ -232,6 +232,57 @@ def test_grouped_gemm_dsv3_full_size_sampled():
     _free()
 
 
+def test_grouped_gemm_dsv3_every_output_against_an_fp32_matmul():
+    """Every one of the 134M outputs at the benchmark's shape (DSV3 routing,
+    256 experts, 7168 -> 4096, tiled weights), checked against an
+    independent fp32 matrix product of each expert's segment (torch on the
+    GPU, full fp32 precision). bf16 products are exact in fp32, so both sums
+    are within gamma_k * sum|x w| of the exact value; with the final bf16
+    rounding: |gpu - ref| <= 2 gamma_k * sum|x w| + 2^-8 |gpu|. The sampled
+    oracle test above pins exact values; this one covers every position."""
+    sh = workloads.EXPERT_SHAPES["dsv3"]
+    wl = workloads.WORKLOADS[sh["workload"]]
+    b = workloads.make_batch(wl)
+    k_in, n_out = sh["k_in"], sh["n_out"]
+    note("dsv3 expert weights (full-size check)")
+    wd = x_to_dev(workloads.expert_weights(wl.E, n_out, k_in, sh["seed"]))
+    wt = tile_expert_weights(wd)
+    disp = MoeDispatcher(wl.nmax, wl.D, wl.E, wl.K, dtype=torch.bfloat16, device=DEV)
+    ids_d, s_d = i32_dev(b["ids"]), f32_dev(b["scores"])
+    lay = disp.layout(ids_d, wl.ntpr)
+    dsp = disp.dispatch(x_to_dev(b["x"]), s_d, ids_d, lay.counts, num_tokens_per_rank=wl.ntpr)
+    out = torch.empty((round_up4(wl.ntpr) * wl.K, n_out), dtype=torch.bfloat16, device=DEV)
+    note("dsv3 grouped_gemm (full-size check)")
+    grouped_gemm(dsp.x_e, wt, lay.offsets, out)
+    sync_or_fail(120)
+    off = lay.offsets.cpu().numpy()
+    gamma = _gamma(k_in)
+    prec = torch.get_float32_matmul_precision()
+    torch.set_float32_matmul_precision("highest")
+    try:
+        worst = 0.0
+        for e in range(wl.E):
+            s0, s1 = int(off[e]), int(off[e + 1])
+            if s1 == s0:
+                continue
+            x = dsp.x_e[s0:s1].float()
+            w = wd[e].float()
+            ref = x @ w.t()
+            mag = x.abs() @ w.abs().t()
+            got = out[s0:s1].float()
+            err = (got - ref).abs()
+            bound = 2 * gamma * mag + 2.0 ** -8 * got.abs()
+            ratio = float((err / bound.clamp_min(1e-30)).max())
+            worst = max(worst, ratio)
+            assert bool((err <= bound).all()), f"expert {e}: error beyond the fp32 bound ({ratio:.3f})"
+        sync_or_fail(120)
+    finally:
+        torch.set_float32_matmul_precision(prec)
+    note(f"dsv3 full-size check: worst error / bound = {worst:.3f}")
+    del disp, wd, wt, out, dsp
+    _free()
+
+
 def test_grouped_gemm_rows_past_4_gib():
     """40960 tokens dispatched (327680 rows, 4.70 GB of x_e), experts
     7168 -> 4096 with tiled weights: rows past byte offset 2^32 are read, and

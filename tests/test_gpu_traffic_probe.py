@@ -80,3 +80,11 @@ def test_sequential_mix_and_streams():
                           3 * torch.ones_like(idx)], dim=1).reshape(-1)
     assert torch.equal(c.cpu(), want_w)
     assert lib.probe_stream(2, a.data_ptr(), b.data_ptr(), n + 16, sink.data_ptr(), _stream()) != 0
+    # kind 3: each KiB of a written to eight consecutive KiB of d
+    m = 1 << 16
+    d = torch.zeros((8 * m // 4,), dtype=torch.int32, device=DEV)
+    assert lib.probe_stream(3, a.data_ptr(), d.data_ptr(), m, sink.data_ptr(), _stream()) == 0
+    sync_or_fail()
+    src = a[: m // 4].view(-1, 256).cpu()
+    assert torch.equal(d.view(-1, 8, 256).cpu(), src[:, None, :].expand(-1, 8, -1))
+    assert lib.probe_stream(3, a.data_ptr(), d.data_ptr(), m + 16, sink.data_ptr(), _stream()) != 0
