@@ -10,7 +10,8 @@
 // the sum to bf16 (nearest even). Rows outside every segment are not written.
 //
 // Work split. A tile is (expert, F output features, up to BT rows of the
-// expert's segment), F = 32 per wavefront. Within an expert, tiles go in
+// expert's segment), F = 32 per 32-feature block of each wavefront. Within an
+// expert, tiles go in
 // blocks of up to 8 row tiles: all feature tiles of a block, each with the
 // block's row tiles fastest. Workgroups are dealt to the 8 XCDs round-robin,
 // so tile numbers are handed out in chunks of consecutive tiles (32, or 16
@@ -25,9 +26,9 @@
 // offsets (a scan of the per-expert tile counts over the 64 lanes) and
 // workgroups without a tile exit.
 //
-// Inside a tile, wavefront w owns features [32w, 32w + 32) and all BT rows:
-// v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand and the
-// token rows as B. Within a step of 64 k, lane half h supplies k = 32h + 8s +
+// Inside a tile, wavefront w owns FB blocks of 32 features, [32 FB w,
+// 32 FB (w + 1)), and all BT rows: v_mfma_f32_32x32x16_bf16 with the weight
+// rows as the A operand and the token rows as B. Within a step of 64 k, lane half h supplies k = 32h + 8s +
 // j (s the instruction, j the element) for both operands: any pairing of k
 // slots gives the same sum. An MFMA fragment puts consecutive lanes on
 // different rows, and loads in that layout run at about a third of the rate
@@ -40,8 +41,14 @@
 //     into a per-wavefront LDS slot (4 wavefronts, 128 features per tile);
 //   - weights in the tiled layout (moe_tile_expert_weights: each 64-lane A
 //     fragment stored as one contiguous KiB) are loaded straight into the
-//     fragment registers, so 16 wavefronts (512 features per tile) share
-//     each row tile and the rows are re-read 4x less often.
+//     fragment registers: 8 wavefronts of two feature blocks (512 features
+//     per tile) share each row tile, so the rows are re-read 4x less often,
+//     and each row fragment read from LDS feeds both blocks' products.
+//     Measured on MI355X (256 experts, 7168 -> 4096, interleaved on one box,
+//     bitwise-equal outputs): 14.15-14.20 against 14.75-14.88 ms at 32768
+//     tokens, 3.33-3.34 against 3.36-3.37 ms at 4096 tokens, compared with
+//     16 wavefronts of one block; the two-block wavefront needs up to 256
+//     VGPRs, so a SIMD holds 2 of them instead of 4.
 // 16-byte chunks sit in LDS at a position XOR-swizzled by the row index, so
 // fragment reads are free of bank conflicts. Loads run kStages steps ahead
 // in a register ring, weights and rows of a step issued together; the loop
@@ -80,16 +87,17 @@ __device__ __forceinline__ void segment(const int32_t* offsets, int32_t e, int32
     s1 = b;
 }
 
-template <int BT, int WAVES, bool TILED>
+template <int BT, int WAVES, int FB, bool TILED>
 __global__ __launch_bounds__(WAVES * 64)
 void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
                          const int32_t* __restrict__ offsets, int32_t E, int32_t max_rows,
                          int32_t chunks, int32_t N, int32_t ftiles, int32_t xcd_chunk,
                          uint8_t* __restrict__ out) {
     constexpr int kThreads = WAVES * 64;
-    constexpr int kFeatures = WAVES * 32;
+    constexpr int kFeatures = WAVES * 32 * FB;
     constexpr int U = BT / 32;                                        // 32-row sub-tiles
     static_assert(U == 2 || U == 4, "row tile of 64 or 128");
+    static_assert(TILED || FB == 1, "row-major weights: one block per wavefront");
     constexpr int UX = (BT * kStepChunks + kThreads - 1) / kThreads;  // row chunks per thread
     // Row buffer plus one dummy chunk per lane for threads past the tile.
     __shared__ v4i xs[2][BT * kStepChunks + 64];
@@ -168,17 +176,20 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
     const int32_t steps_all = (chunks + kStepChunks - 1) / kStepChunks;
 
     // Weights. Tiled: [E][ceil(N/32)][steps][4][64 lanes] chunks, this
-    // wavefront's 32-feature block (clamped into range; the extra features
+    // wavefront's FB 32-feature blocks (clamped into range; the extra features
     // are never stored). Row-major: lane l loads rows (l >> 3) + 8j, chunk
     // l & 7 of the wavefront's 32 rows (features past N read row N-1).
-    const v4i* wt = nullptr;
+    const v4i* wt[FB] = {};
     const v4i* wrow[4];
     int32_t wslot[4];
     v4i* wbuf = ws[TILED ? 0 : wave];
     if constexpr (TILED) {
         const int32_t nb = (N + 31) / 32;
-        const int32_t fb = min(f0 / 32 + wave, nb - 1);
-        wt = w + ((int64_t(e) * nb + fb) * steps_all) * 4 * 64 + lane;
+#pragma unroll
+        for (int b = 0; b < FB; ++b) {
+            const int32_t blk = min(f0 / 32 + wave * FB + b, nb - 1);
+            wt[b] = w + ((int64_t(e) * nb + blk) * steps_all) * 4 * 64 + lane;
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -210,21 +221,23 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
     // body stays branch-free.
     auto run = [&](auto sub) {
         constexpr int UU = decltype(sub)::value;
-        f32x16 acc[UU];
+        f32x16 acc[FB][UU];
 #pragma unroll
-        for (int u = 0; u < UU; ++u)
+        for (int b = 0; b < FB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
+            for (int u = 0; u < UU; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][u][r] = 0.0f;
 
         // One step: rows (and row-major weights) of the step, already in
-        // registers, to LDS; then the 4 x UU matrix-core products.
-        auto mma_step = [&](int buf_id, const v4i (&wv)[4], const v4i (&xv)[UX], auto&& after_barrier) {
+        // registers, to LDS; then the 4 x UU x FB matrix-core products.
+        auto mma_step = [&](int buf_id, const v4i (&wv)[FB][4], const v4i (&xv)[UX], auto&& after_barrier) {
             v4i* buf = xs[buf_id];
 #pragma unroll
             for (int j = 0; j < UX; ++j) buf[xslot[j]] = xv[j];
             if constexpr (!TILED) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wbuf[wslot[j]] = wv[j];
+                for (int j = 0; j < 4; ++j) wbuf[wslot[j]] = wv[0][j];
             }
             __syncthreads();
             after_barrier();
@@ -239,49 +252,57 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
             bf16x8 bcur = bread(0, 0);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                bf16x8 a;
-                if constexpr (TILED)
-                    a = as_bf16x8(wv[s]);
-                else
-                    a = as_bf16x8(wbuf[i * kStepChunks + ((4 * h + s) ^ swz(i))]);
+                bf16x8 a[FB];
+#pragma unroll
+                for (int b = 0; b < FB; ++b) {
+                    if constexpr (TILED)
+                        a[b] = as_bf16x8(wv[b][s]);
+                    else
+                        a[b] = as_bf16x8(wbuf[i * kStepChunks + ((4 * h + s) ^ swz(i))]);
+                }
 #pragma unroll
                 for (int u = 0; u < UU; ++u) {
                     const int nu = u + 1 < UU ? u + 1 : 0;
                     const int ns = u + 1 < UU ? s : s + 1;
                     bf16x8 bnext = bcur;
                     if (ns < 4) bnext = bread(ns, nu);
-                    acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bcur, acc[u], 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < FB; ++b)
+                        acc[b][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[b], bcur, acc[b][u], 0, 0, 0);
                     bcur = bnext;
                 }
             }
             if constexpr (TILED) {
                 // Scheduling groups that keep that order: two LDS reads
-                // before the first product, then one read per product (mask
-                // 0x100: LDS reads, 0x008: matrix-core instructions). With
-                // tiled weights the step's only LDS reads are the 4 * UU row
-                // fragments. Measured on MI355X at 32768 tokens x 7168 ->
-                // 4096: 13.9 against 14.2-14.4 ms, results bitwise equal.
+                // before the first products, then one read per FB products
+                // (mask 0x100: LDS reads, 0x008: matrix-core instructions).
+                // With tiled weights the step's only LDS reads are the 4 * UU
+                // row fragments. Measured on MI355X at 32768 tokens x 7168 ->
+                // 4096 (one block per wavefront): 13.9 against 14.2-14.4 ms,
+                // results bitwise equal.
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
                 for (int q = 0; q < 4 * UU - 2; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, FB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * FB, 0);
             }
         };
 
         const int32_t full = chunks / kStepChunks;
-        v4i wr[kStages][4];
+        v4i wr[kStages][FB][4];
         v4i xr[kStages][UX];
-        auto load_w = [&](int32_t step, v4i (&dst)[4]) {
+        auto load_w = [&](int32_t step, v4i (&dst)[FB][4]) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (TILED)
-                    dst[j] = wt[(step * 4 + j) * 64];
-                else
-                    dst[j] = wrow[j][step * kStepChunks];
-            }
+            for (int b = 0; b < FB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (TILED)
+                        dst[b][j] = wt[b][(step * 4 + j) * 64];
+                    else
+                        dst[b][j] = wrow[j][step * kStepChunks];
+                }
         };
         auto load_x = [&](int32_t step, v4i (&dst)[UX]) {
 #pragma unroll
@@ -317,17 +338,19 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
             const int32_t c0 = done * kStepChunks;
             const int32_t last = chunks - 1;
             const v4i zero = {0, 0, 0, 0};
-            v4i wv[4], xv[UX];
+            v4i wv[FB][4], xv[UX];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (TILED) {
-                    wv[j] = wt[(done * 4 + j) * 64];
-                } else {
-                    const int32_t c = c0 + (lane & 7);
-                    const v4i v = wrow[j][min(c, last) - (lane & 7)];
-                    wv[j] = c <= last ? v : zero;
+            for (int b = 0; b < FB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (TILED) {
+                        wv[b][j] = wt[b][(done * 4 + j) * 64];
+                    } else {
+                        const int32_t c = c0 + (lane & 7);
+                        const v4i v = wrow[j][min(c, last) - (lane & 7)];
+                        wv[b][j] = c <= last ? v : zero;
+                    }
                 }
-            }
 #pragma unroll
             for (int j = 0; j < UX; ++j) {
                 const int32_t c = c0 + xc[j];
@@ -337,22 +360,26 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
             mma_step(done & 1, wv, xv, [] {});
         }
 
-        // acc[u][4q + t] is out[row u*32 + i][feature 32w + 8q + 4h + t].
+        // acc[b][u][4q + t] is out[row u*32 + i][feature 32(FB w + b) + 8q +
+        // 4h + t].
 #pragma unroll
-        for (int u = 0; u < UU; ++u) {
-            const int r = u * 32 + i;
-            if (r >= nrows) continue;
-            uint8_t* orow = out + (int64_t(row0 + r) * N) * 2;
+        for (int b = 0; b < FB; ++b)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int32_t col = f0 + wave * 32 + 8 * q + 4 * h;
-                if (col >= N) continue;
-                uint2 v;
-                v.x = f32_to_bf16_bits(acc[u][4 * q]) | (f32_to_bf16_bits(acc[u][4 * q + 1]) << 16);
-                v.y = f32_to_bf16_bits(acc[u][4 * q + 2]) | (f32_to_bf16_bits(acc[u][4 * q + 3]) << 16);
-                *reinterpret_cast<uint2*>(orow + int64_t(col) * 2) = v;
+            for (int u = 0; u < UU; ++u) {
+                const int r = u * 32 + i;
+                if (r >= nrows) continue;
+                uint8_t* orow = out + (int64_t(row0 + r) * N) * 2;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int32_t col = f0 + (wave * FB + b) * 32 + 8 * q + 4 * h;
+                    if (col >= N) continue;
+                    const f32x16& c = acc[b][u];
+                    uint2 v;
+                    v.x = f32_to_bf16_bits(c[4 * q]) | (f32_to_bf16_bits(c[4 * q + 1]) << 16);
+                    v.y = f32_to_bf16_bits(c[4 * q + 2]) | (f32_to_bf16_bits(c[4 * q + 3]) << 16);
+                    *reinterpret_cast<uint2*>(orow + int64_t(col) * 2) = v;
+                }
             }
-        }
     };
     const int usub = (nrows + 31) / 32;
     if (usub <= 1)
@@ -391,14 +418,16 @@ void tile_weights_kernel(const v4i* __restrict__ src, int32_t N, int32_t chunks,
     dst[q] = v;
 }
 
-template <int BT, int WAVES, bool TILED>
+template <int BT, int WAVES, int FB, bool TILED>
 hipError_t launch_bt(const GroupedGemmArgs& a, hipStream_t stream) {
-    const int64_t grid = grouped_gemm_grid(a.max_rows, a.E, a.N, BT, WAVES * 32);
-    hipLaunchKernelGGL((grouped_gemm_kernel<BT, WAVES, TILED>), dim3(static_cast<uint32_t>(grid)),
+    constexpr int32_t kFeatures = WAVES * 32 * FB;
+    static_assert(kFeatures == gemm_tile_features(TILED), "tile width as the host sizes it");
+    const int64_t grid = grouped_gemm_grid(a.max_rows, a.E, a.N, BT, kFeatures);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BT, WAVES, FB, TILED>), dim3(static_cast<uint32_t>(grid)),
                        dim3(WAVES * 64), 0, stream, static_cast<const v4i*>(a.x_e),
                        static_cast<const v4i*>(a.w), a.offsets, a.E,
                        static_cast<int32_t>(a.max_rows), a.Kd / 8, a.N,
-                       static_cast<int32_t>((a.N + WAVES * 32 - 1) / (WAVES * 32)),
+                       static_cast<int32_t>((a.N + kFeatures - 1) / kFeatures),
                        gemm_xcd_chunk(a.max_rows, a.E), static_cast<uint8_t*>(a.out));
     return hipGetLastError();
 }
@@ -409,14 +438,14 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     if (a.max_rows <= 0) return hipSuccess;
     if (a.tiled) {
         switch (a.row_tile) {
-            case 64: return launch_bt<64, kGemmWavesTiled, true>(a, stream);
-            case 128: return launch_bt<128, kGemmWavesTiled, true>(a, stream);
+            case 64: return launch_bt<64, kGemmWavesTiled, kGemmBlocksTiled, true>(a, stream);
+            case 128: return launch_bt<128, kGemmWavesTiled, kGemmBlocksTiled, true>(a, stream);
             default: return hipErrorInvalidValue;
         }
     }
     switch (a.row_tile) {
-        case 64: return launch_bt<64, kGemmWavesRowMajor, false>(a, stream);
-        case 128: return launch_bt<128, kGemmWavesRowMajor, false>(a, stream);
+        case 64: return launch_bt<64, kGemmWavesRowMajor, 1, false>(a, stream);
+        case 128: return launch_bt<128, kGemmWavesRowMajor, 1, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

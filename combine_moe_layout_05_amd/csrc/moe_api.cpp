@@ -586,8 +586,7 @@ int moe_grouped_gemm(const void* d_x_expert, const void* d_weights, const int32_
         row_tile = max_rows >= int64_t(64) * num_experts ? moe::kGemmRowTileLarge
                                                          : moe::kGemmRowTileSmall;
     const bool tiled = weight_layout == MOE_WEIGHTS_TILED;
-    const int32_t features =
-        32 * (tiled ? moe::kGemmWavesTiled : moe::kGemmWavesRowMajor);
+    const int32_t features = moe::gemm_tile_features(tiled);
     if (moe::grouped_gemm_grid(max_rows, num_experts, n_out, row_tile, features) > INT32_MAX)
         return MOE_ERR_INVALID_ARG;
     moe::GroupedGemmArgs a;

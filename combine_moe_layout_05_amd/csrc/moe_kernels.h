@@ -228,10 +228,17 @@ inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t
 }
 constexpr int kGemmRowTileSmall = 64;
 constexpr int kGemmRowTileLarge = 128;
-// Wavefronts per workgroup (32 output features each): row-major weights are
-// staged through LDS per wavefront; tiled weights go straight to registers.
+// Wavefronts per workgroup and 32-feature blocks per wavefront: row-major
+// weights are staged through LDS per wavefront (one block each); tiled
+// weights go straight to registers, two blocks per wavefront, so each row
+// fragment read from LDS feeds two matrix-core products.
 constexpr int kGemmWavesRowMajor = 4;
-constexpr int kGemmWavesTiled = 16;
+constexpr int kGemmWavesTiled = 8;
+constexpr int kGemmBlocksTiled = 2;
+// Output features per workgroup tile.
+constexpr int32_t gemm_tile_features(bool tiled) {
+    return tiled ? 32 * kGemmWavesTiled * kGemmBlocksTiled : 32 * kGemmWavesRowMajor;
+}
 
 struct GroupedGemmArgs {
     const void* x_e;        // [max_rows][Kd] bf16
