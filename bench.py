@@ -140,6 +140,10 @@ def parse_args():
                    help="1/2: force the one- or two-launch layout; -1 or 0: by size (default)")
     p.add_argument("--dispatch-store-burst", type=int, default=0, choices=[0, 1, 2],
                    help="1/2: back-to-back or paced dispatch stores; 0: library default (paced)")
+    p.add_argument("--combine-backward-store", type=int, default=0, choices=[0, 1, 2],
+                   help="stores of dL/dy_e in moe_combine_backward: 1 streaming, 2 ordinary, "
+                        "0 the library's choice (streaming when the buffer exceeds the "
+                        "last-level cache)")
     p.add_argument("--backward", type=int, default=0,
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--expert-iters", type=int, default=10,
@@ -651,7 +655,8 @@ def main() -> int:
                     bool(args.combine_nontemporal) if args.combine_nontemporal >= 0 else None,
                     args.dispatch_block_waves, args.combine_block_waves,
                     bool(args.combine_store_nontemporal) if args.combine_store_nontemporal >= 0
-                    else None, args.layout_launches, args.dispatch_store_burst)
+                    else None, args.layout_launches, args.dispatch_store_burst,
+                    args.combine_backward_store)
     tuning = disp.get_tuning()
     ntpr = w.ntpr
     step = make_step(disp, x, ids, s, ntpr)
@@ -787,6 +792,9 @@ def main() -> int:
         cb = float(np.mean([e[0].elapsed_time(e[1]) for e in bev[2:]])) * 1e3
         db = float(np.mean([e[1].elapsed_time(e[2]) for e in bev[2:]])) * 1e3
         backward = {"combine_backward_us": round(cb, 2), "dispatch_backward_us": round(db, 2),
+                    "both_us": round(cb + db, 2),
+                    "combine_backward_store": "streaming" if tuning["combine_backward_store"] == 1
+                    else "ordinary",
                     "combine_backward_gbps": round(bytes_per_token(w, "combine_backward") * w.T
                                                    / (cb * 1e-6) / 1e9, 1),
                     "dispatch_backward_gbps": round(bytes_per_token(w, "dispatch_backward") * w.T

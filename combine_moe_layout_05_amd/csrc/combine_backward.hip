@@ -23,7 +23,9 @@
 // deterministic; it differs from plain left-to-right order, which stays
 // within the fp32 summation error bound of the dot product. The launch has
 // kTailBlocks more workgroups than tokens; they store zeros into the rows
-// [*total_rows, row_limit), a row per workgroup per turn.
+// [*total_rows, row_limit), a row per workgroup per turn. With NTS the dL/dy_e
+// rows are written with streaming stores (the context picks them for buffers
+// far beyond the last-level cache); results are the same bits either way.
 #include "moe_kernels.h"
 #include "moe_lanes.h"
 
@@ -35,7 +37,15 @@ namespace {
 // Workgroups of the launch that zero the rows past the true total.
 constexpr int32_t kTailBlocks = 512;
 
-template <int K, bool BF16>
+template <bool NTS>
+__device__ __forceinline__ void put_row(v4i* p, v4i v) {
+    if constexpr (NTS)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+template <int K, bool BF16, bool NTS>
 __global__ __launch_bounds__(kMaxBlockThreads)
 void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restrict__ y_e,
                              const int32_t* __restrict__ row_map,
@@ -62,7 +72,8 @@ void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restri
         const v4i zero = {0, 0, 0, 0};
         for (int64_t r = lo + (t - T); r < row_limit; r += kTailBlocks) {
             v4i* dst = grad_y_e + r * chunks;
-            for (int32_t c = tid; c < chunks; c += static_cast<int32_t>(blockDim.x)) dst[c] = zero;
+            for (int32_t c = tid; c < chunks; c += static_cast<int32_t>(blockDim.x))
+                put_row<NTS>(dst + c, zero);
         }
         return;
     }
@@ -109,7 +120,7 @@ void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restri
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     if (!decltype(every)::value && row[k] < 0) continue;
-                    grad_y_e[int64_t(row[k]) * chunks + c] = L::scale(s[k], gv);
+                    put_row<NTS>(grad_y_e + int64_t(row[k]) * chunks + c, L::scale(s[k], gv));
                     dot[k] = L::dot_into(dot[k], gv, yv[k]);
                 }
             }
@@ -142,7 +153,9 @@ hipError_t launch_k(const CombineBackwardArgs& a, hipStream_t stream) {
     if (waves > kMaxBlockWaves) waves = kMaxBlockWaves;
     // Token workgroups first, then the tail workgroups (only when asked for).
     const int64_t blocks = int64_t(a.T) + (a.total_rows ? kTailBlocks : 0);
-    hipLaunchKernelGGL((combine_backward_kernel<K, BF16>), dim3(static_cast<uint32_t>(blocks)),
+    auto kernel = a.store_nontemporal ? combine_backward_kernel<K, BF16, true>
+                                      : combine_backward_kernel<K, BF16, false>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)),
                        dim3(64 * waves), 0, stream, static_cast<const v4i*>(a.grad_y),
                        static_cast<const v4i*>(a.y_e), a.row_map, a.scores, a.T, a.chunks,
                        a.row_limit, a.total_rows, static_cast<v4i*>(a.grad_y_e), a.grad_s);

@@ -186,6 +186,7 @@ struct CombineBackwardArgs {
     float* grad_s;          // [T][K]
     const int32_t* total_rows = nullptr;  // device; rows [*total_rows, row_limit) of
                                           // grad_y_e get +0.0 (nullptr: not written)
+    bool store_nontemporal = false;       // streaming stores of grad_y_e
 };
 hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t stream);
 

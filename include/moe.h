@@ -406,8 +406,12 @@ int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t 
  * slots, the default), 0 keeps the current value. dispatch_store_burst 1
  * issues each wavefront's K row stores back to back, 2 issues each after the
  * previous one has completed (the default), 0 keeps the current value; it
- * applies to the default one-chunk-per-lane shape. Results do not depend on
- * any of these. Pure host. */
+ * applies to the default one-chunk-per-lane shape. combine_backward_store 1
+ * writes moe_combine_backward's dL/dy_e rows with streaming stores, 2 with
+ * ordinary ones, 0 keeps the current value; by default they stream when the
+ * context's dL/dy_e buffer is larger than 1 GiB (four times the 256 MB
+ * last-level cache).
+ * Results do not depend on any of these. Pure host. */
 typedef struct moe_tuning {
     int32_t dispatch_segments;
     int32_t combine_segments;
@@ -418,6 +422,7 @@ typedef struct moe_tuning {
     int32_t combine_store_nontemporal;  /* streaming stores of y; -1 keeps */
     int32_t layout_launches;            /* 1, 2, or -1 (by size); 0 keeps */
     int32_t dispatch_store_burst;       /* 1 back to back, 2 paced; 0 keeps */
+    int32_t combine_backward_store;     /* 1 streaming, 2 ordinary; 0 keeps */
 } moe_tuning;
 int moe_set_tuning(moe_ctx *ctx, const moe_tuning *tuning);
 int moe_get_tuning(const moe_ctx *ctx, moe_tuning *out);

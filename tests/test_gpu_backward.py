@@ -126,6 +126,8 @@ def test_backward_padded(T):
 @pytest.mark.parametrize("name", ["dsv3", "graph"])
 def test_backward_full_shapes(name):
     w, b, g, disp = _case(name)
+    # dL/dy_e of 470 / 537 MB: ordinary stores by default
+    assert disp.get_tuning()["combine_backward_store"] == 2
     note(f"backward {name} T={w.T}")
     gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, w.T, w.ntpr)
     ob = oracle_backward(b["x"], b["ids"], b["scores"], g, w.T, w.ntpr, w.E, w.K)
@@ -151,6 +153,7 @@ def test_backward_past_4_gib():
     b = workloads.make_batch(w)
     g = _grad_y(w.T, w.D, w.dtype, 77)
     disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV, backward=True)
+    assert disp.get_tuning()["combine_backward_store"] == 1     # 4.70 GB: streaming stores
     note("backward past 4 GiB: GPU")
     gb = gpu_backward(disp, b["x"], b["ids"], b["scores"], g, w.T, w.ntpr)
     del disp
@@ -264,19 +267,24 @@ def test_backward_poisoned_workspace_and_flag():
     _free()
 
 
+@pytest.mark.parametrize("store", [1, 2])
 @pytest.mark.parametrize("T", [614, 2047, 0])
-def test_backward_total_zeroes_the_rows_no_slot_reaches(T):
+def test_backward_total_zeroes_the_rows_no_slot_reaches(T, store):
     """With the device-side total, moe_combine_backward writes +0.0 into the
     dL/dy_e rows [total, round_up4(ntpr) * K), which no slot reaches, and
     leaves the rows past the current capacity alone (a poisoned workspace
-    shows both). The slots' rows stay bitwise equal to the oracle."""
+    shows both). The slots' rows stay bitwise equal to the oracle, with
+    streaming (store=1) and ordinary (store=2) stores of dL/dy_e."""
     w = workloads.WORKLOADS["padded"]
     b = workloads.make_batch(w)
     g = _grad_y(2048, w.D, "bf16", 8)
     disp = MoeDispatcher(w.nmax, w.D, w.E, w.K, dtype=torch.bfloat16, device=DEV, backward=True)
+    assert disp.get_tuning()["combine_backward_store"] == 2     # 134 MB of dL/dy_e: cached
+    disp.set_tuning(combine_backward_store=store)
+    assert disp.get_tuning()["combine_backward_store"] == store
     disp.workspace.fill_(0xFF)
     sync_or_fail()
-    note(f"backward with total, poisoned workspace, T={T}")
+    note(f"backward with total, poisoned workspace, T={T}, store={store}")
     ids_d, s_d = i32_dev(b["ids"][:T]), f32_dev(b["scores"][:T])
     x_d = x_to_dev(b["x"][:T]) if T else torch.empty((0, w.D), dtype=torch.bfloat16, device=DEV)
     g_d = x_to_dev(g[:T]) if T else torch.empty((0, w.D), dtype=torch.bfloat16, device=DEV)

@@ -297,6 +297,7 @@ def test_tuning_roundtrip_and_limits(lib):
     assert t.combine_store_nontemporal == 0          # 58.7 MB output: stays cacheable
     assert t.layout_launches == -1                   # layout launches chosen by size
     assert t.dispatch_store_burst == 2               # dispatch stores paced by default
+    assert t.combine_backward_store == 2             # 470 MB of dL/dy_e: ordinary stores
     assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 2))) == L.MOE_OK
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.layout_launches == 2
     assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 1))) == L.MOE_OK
@@ -314,9 +315,21 @@ def test_tuning_roundtrip_and_limits(lib):
             t.dispatch_block_waves, t.combine_block_waves, t.combine_store_nontemporal) == \
         (4, 3, 0, 0, 2, 16, 1)
     assert t.layout_launches == 1                    # 0 keeps the current value
+    t.combine_backward_store = 1
+    assert lib.moe_set_tuning(ctx, C.byref(t)) == L.MOE_OK
+    t.combine_backward_store = 0                     # 0 keeps the current value
+    assert lib.moe_set_tuning(ctx, C.byref(t)) == L.MOE_OK
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_backward_store == 1
+    for v in (3, -1):
+        t.combine_backward_store = v
+        assert lib.moe_set_tuning(ctx, C.byref(t)) == L.MOE_ERR_INVALID_ARG
+    lib.moe_destroy(ctx)
+    ctx, _, _ = _ctx(lib, _cfg(nmax=256, D=1024))    # 4 MB of dL/dy_e: cached
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_backward_store == 2
     lib.moe_destroy(ctx)
     ctx, _, _ = _ctx(lib, _cfg(nmax=32768))         # 470 MB output: streamed
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_store_nontemporal == 1
+    assert t.combine_backward_store == 1             # 3.76 GB of dL/dy_e: streamed
     for bad in ((17, 1, 0, 0, 0, 0, 0), (-1, 1, 0, 0, 0, 0, 0), (1, 1, 0, 0, 17, 0, 0),
                 (1, 1, 0, 0, 0, -2, 0), (1, 1, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, -2),
                 (1, 1, 0, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, 0, -1)):
