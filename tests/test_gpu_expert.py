@@ -72,6 +72,7 @@ SMALL = [  # E, counts (None = random), k_in, n_out
     (16, [0] * 7 + [300] + [0] * 8, 520, 136),  # one expert with every row
     (300, None, 64, 128),                   # more experts than lanes
     (4, [900, 0, 1300, 300], 200, 72),      # >= 512 rows per expert: tiles dealt in chunks
+    (3, [40, 0, 200], 128, 1000),           # a second, partial 512-feature tile
 ]
 
 
