@@ -144,6 +144,9 @@ def parse_args():
                    help="stores of dL/dy_e in moe_combine_backward: 1 streaming, 2 ordinary, "
                         "0 the library's choice (streaming when the buffer exceeds the "
                         "last-level cache)")
+    p.add_argument("--dispatch-x-nontemporal", type=int, default=0, choices=[0, 1, 2],
+                   help="loads of x in dispatch: 1 streaming, 2 ordinary, 0 the library's choice "
+                        "(streaming when the expert buffer is 1-4x the last-level cache)")
     p.add_argument("--backward", type=int, default=0,
                    help="also time moe_combine_backward and moe_dispatch_backward (steps)")
     p.add_argument("--expert-iters", type=int, default=10,
@@ -656,7 +659,7 @@ def main() -> int:
                     args.dispatch_block_waves, args.combine_block_waves,
                     bool(args.combine_store_nontemporal) if args.combine_store_nontemporal >= 0
                     else None, args.layout_launches, args.dispatch_store_burst,
-                    args.combine_backward_store)
+                    args.combine_backward_store, args.dispatch_x_nontemporal)
     tuning = disp.get_tuning()
     ntpr = w.ntpr
     step = make_step(disp, x, ids, s, ntpr)

@@ -55,7 +55,8 @@ class MoeTuning(C.Structure):
                 ("dispatch_nontemporal", _i32), ("combine_nontemporal", _i32),
                 ("dispatch_block_waves", _i32), ("combine_block_waves", _i32),
                 ("combine_store_nontemporal", _i32), ("layout_launches", _i32),
-                ("dispatch_store_burst", _i32), ("combine_backward_store", _i32)]
+                ("dispatch_store_burst", _i32), ("combine_backward_store", _i32),
+                ("dispatch_x_nontemporal", _i32)]
 
 
 SIGNATURES = {

@@ -53,7 +53,19 @@ __device__ __forceinline__ v4i transform(float s, v4i v) {
 // The copy of one wavefront's item: its K rows from the staged row map, the
 // row chunk(s) stored K times, and (first segment) the slots' scores. BURST
 // (single-chunk shape only): the K stores issue back to back.
-template <int K, bool NT, bool SINGLE, int MODE, bool BURST>
+// A chunk of a token row of x: ordinary load, or streaming (NTX) so that x,
+// read exactly once, does not take cache space from the expert rows written
+// next to it. A template parameter: with a runtime flag the compiler merges
+// the two loads of one address into a single ordinary load.
+template <bool NTX>
+__device__ __forceinline__ v4i load_x(const v4i* p) {
+    if constexpr (NTX)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <int K, bool NT, bool SINGLE, int MODE, bool BURST, bool NTX>
 __device__ __forceinline__ void copy_rows(const float* __restrict__ scores,
                                           int32_t chunks, v4i* __restrict__ x_e,
                                           float* __restrict__ s_e, const int32_t* tile_rows,
@@ -111,7 +123,7 @@ __device__ __forceinline__ void copy_rows(const float* __restrict__ scores,
         for (; c0 + 64 * U <= c_end; c0 += 64 * U) {
             v4i v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = src[c0 + u * 64 + lane];
+            for (int u = 0; u < U; ++u) v[u] = load_x<NTX>(src + c0 + u * 64 + lane);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 if (row[k] < 0) continue;
@@ -124,7 +136,7 @@ __device__ __forceinline__ void copy_rows(const float* __restrict__ scores,
         for (; c0 < c_end; c0 += 64) {
             const int32_t c = c0 + lane;
             if (c >= c_end) break;
-            const v4i v = src[c];
+            const v4i v = load_x<NTX>(src + c);
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 if (row[k] >= 0) put<NT>(x_e + int64_t(row[k]) * chunks + c, transform<MODE>(s[k], v));
@@ -152,7 +164,7 @@ struct RankArgs {
 // copied in groups of U chunks per lane, then one chunk at a time. RANK: the
 // workgroup computes its tokens' rows (and writes them to row_map and
 // src_map) instead of reading row_map.
-template <int K, bool NT, bool SINGLE, int MODE, bool RANK, bool BURST>
+template <int K, bool NT, bool SINGLE, int MODE, bool RANK, bool BURST, bool NTX>
 __global__ __launch_bounds__(kMaxBlockThreads)
 void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores,
                      const int32_t* __restrict__ row_map, int32_t T, int32_t chunks,
@@ -187,7 +199,7 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     float early_score = 0.0f;
     if constexpr (SINGLE) {
         const int32_t c = c_begin + lane;
-        if (live && c < c_end) early = src[c];
+        if (live && c < c_end) early = load_x<NTX>(src + c);
         if (live && seg == 0 && lane < K) early_score = scores[t * K + lane];
     }
     // RANK: the row this thread records in row_map / src_map after the copy
@@ -253,7 +265,7 @@ void dispatch_kernel(const v4i* __restrict__ x, const float* __restrict__ scores
     __syncthreads();
 
     if (live)
-        copy_rows<K, NT, SINGLE, MODE, BURST>(scores, chunks, x_e, s_e, tile_rows, tile_scores, t,
+        copy_rows<K, NT, SINGLE, MODE, BURST, NTX>(scores, chunks, x_e, s_e, tile_rows, tile_scores, t,
                                               t_first, seg, c_begin, c_end, src, early,
                                               early_score, lane);
     if constexpr (RANK) {
@@ -271,19 +283,24 @@ hipError_t launch_kb(const DispatchArgs& a, const RankArgs& rk, int32_t segments
     const int64_t items = int64_t(a.T) * segments;
     const int64_t blocks = (items + a.block_waves - 1) / a.block_waves;
     const bool single = seg_chunks == 64;
-    decltype(&dispatch_kernel<K, false, true, kCopy, RANK, BURST>) kernel;
+    decltype(&dispatch_kernel<K, false, true, kCopy, RANK, BURST, false>) kernel;
     // BURST only changes the single-chunk copy; the multi-chunk copy has one
-    // instantiation (BURST = false).
+    // instantiation (BURST = false). Streaming loads of x (NTX) are offered
+    // with the bit copy and ordinary stores.
     if (a.scaled) {  // streaming stores are not offered with the scores applied
-        kernel = a.bf16 ? (single ? dispatch_kernel<K, false, true, kScaleBF16, RANK, BURST>
-                                  : dispatch_kernel<K, false, false, kScaleBF16, RANK, false>)
-                        : (single ? dispatch_kernel<K, false, true, kScaleF32, RANK, BURST>
-                                  : dispatch_kernel<K, false, false, kScaleF32, RANK, false>);
+        kernel = a.bf16 ? (single ? dispatch_kernel<K, false, true, kScaleBF16, RANK, BURST, false>
+                                  : dispatch_kernel<K, false, false, kScaleBF16, RANK, false, false>)
+                        : (single ? dispatch_kernel<K, false, true, kScaleF32, RANK, BURST, false>
+                                  : dispatch_kernel<K, false, false, kScaleF32, RANK, false, false>);
+    } else if (a.nontemporal) {
+        kernel = single ? dispatch_kernel<K, true, true, kCopy, RANK, BURST, false>
+                        : dispatch_kernel<K, true, false, kCopy, RANK, false, false>;
+    } else if (a.load_nontemporal) {
+        kernel = single ? dispatch_kernel<K, false, true, kCopy, RANK, BURST, true>
+                        : dispatch_kernel<K, false, false, kCopy, RANK, false, true>;
     } else {
-        kernel = a.nontemporal ? (single ? dispatch_kernel<K, true, true, kCopy, RANK, BURST>
-                                         : dispatch_kernel<K, true, false, kCopy, RANK, false>)
-                               : (single ? dispatch_kernel<K, false, true, kCopy, RANK, BURST>
-                                         : dispatch_kernel<K, false, false, kCopy, RANK, false>);
+        kernel = single ? dispatch_kernel<K, false, true, kCopy, RANK, BURST, false>
+                        : dispatch_kernel<K, false, false, kCopy, RANK, false, false>;
     }
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * a.block_waves), 0,
                        stream, static_cast<const v4i*>(a.x), a.scores, a.row_map, a.T,

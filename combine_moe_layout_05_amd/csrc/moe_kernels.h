@@ -131,6 +131,7 @@ struct DispatchArgs {
     bool scaled;            // x_e[r] = scores[t][k] * x[t] instead of a bit copy
     bool bf16;              // element type (used when scaled)
     bool store_burst = false;  // single-chunk copies: K stores back to back
+    bool load_nontemporal = false;  // streaming loads of x
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 

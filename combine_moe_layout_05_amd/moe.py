@@ -496,19 +496,20 @@ class MoeDispatcher:
                    dispatch_block_waves: int = 0, combine_block_waves: int = 0,
                    combine_store_nontemporal: Optional[bool] = None,
                    layout_launches: int = 0, dispatch_store_burst: int = 0,
-                   combine_backward_store: int = 0) -> None:
+                   combine_backward_store: int = 0, dispatch_x_nontemporal: int = 0) -> None:
         """Launch shape only; results never depend on it. 0 / None keep the
         current value; layout_launches 1 or 2 forces one or two layout
         launches (-1 chooses by size); dispatch_store_burst 1 or 2 selects
         back-to-back or paced dispatch stores; combine_backward_store 1 or 2
-        selects streaming or ordinary stores of dL/dy_e."""
+        selects streaming or ordinary stores of dL/dy_e; dispatch_x_nontemporal
+        1 or 2 selects streaming or ordinary loads of x in dispatch."""
         cur = self.get_tuning()
         dnt = cur["dispatch_nontemporal"] if dispatch_nontemporal is None else dispatch_nontemporal
         cnt = cur["combine_nontemporal"] if combine_nontemporal is None else combine_nontemporal
         snt = -1 if combine_store_nontemporal is None else int(combine_store_nontemporal)
         t = L.MoeTuning(dispatch_segments, combine_segments, int(dnt), int(cnt),
                         dispatch_block_waves, combine_block_waves, snt, layout_launches,
-                        dispatch_store_burst, combine_backward_store)
+                        dispatch_store_burst, combine_backward_store, dispatch_x_nontemporal)
         L.check(self._lib.moe_set_tuning(self._ctx, C.byref(t)), "moe_set_tuning")
 
     def get_tuning(self) -> dict:
@@ -522,4 +523,5 @@ class MoeDispatcher:
                 "combine_store_nontemporal": bool(t.combine_store_nontemporal),
                 "layout_launches": t.layout_launches,
                 "dispatch_store_burst": t.dispatch_store_burst,
-                "combine_backward_store": t.combine_backward_store}
+                "combine_backward_store": t.combine_backward_store,
+                "dispatch_x_nontemporal": t.dispatch_x_nontemporal}

@@ -410,7 +410,11 @@ int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t 
  * writes moe_combine_backward's dL/dy_e rows with streaming stores, 2 with
  * ordinary ones, 0 keeps the current value; by default they stream when the
  * context's dL/dy_e buffer is larger than 1 GiB (four times the 256 MB
- * last-level cache).
+ * last-level cache). dispatch_x_nontemporal 1 makes dispatch read the rows
+ * of x with streaming loads (the bit copy with ordinary stores: moe_dispatch
+ * and moe_layout_dispatch), 2 with ordinary ones, 0 keeps the current value;
+ * by default they stream when the context's expert buffer is larger than
+ * the last-level cache and at most four times it.
  * Results do not depend on any of these. Pure host. */
 typedef struct moe_tuning {
     int32_t dispatch_segments;
@@ -423,6 +427,7 @@ typedef struct moe_tuning {
     int32_t layout_launches;            /* 1, 2, or -1 (by size); 0 keeps */
     int32_t dispatch_store_burst;       /* 1 back to back, 2 paced; 0 keeps */
     int32_t combine_backward_store;     /* 1 streaming, 2 ordinary; 0 keeps */
+    int32_t dispatch_x_nontemporal;     /* 1 streaming, 2 ordinary; 0 keeps */
 } moe_tuning;
 int moe_set_tuning(moe_ctx *ctx, const moe_tuning *tuning);
 int moe_get_tuning(const moe_ctx *ctx, moe_tuning *out);

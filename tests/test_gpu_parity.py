@@ -348,6 +348,40 @@ def test_dispatch_store_schedules(name, T, burst):
     _free()
 
 
+@pytest.mark.parametrize("xnt", [1, 2])
+@pytest.mark.parametrize("name,T", [("padded", 2047), ("dsv3", 4096), ("graph", 8192)])
+def test_dispatch_x_loads(name, T, xnt):
+    """Streaming (xnt=1) and ordinary (xnt=2) loads of x in dispatch give the
+    oracle's buffers bit for bit."""
+    w = workloads.WORKLOADS[name]
+    b = workloads.make_batch(w)
+    disp = _dispatcher(w)
+    default = disp.get_tuning()["dispatch_x_nontemporal"]
+    # expert buffer 134 MB (padded): ordinary; 470 / 537 MB: streaming
+    assert default == (2 if name == "padded" else 1)
+    disp.set_tuning(dispatch_x_nontemporal=xnt)
+    assert disp.get_tuning()["dispatch_x_nontemporal"] == xnt
+    _full_check(disp, b, T, w.ntpr, w.E, w.K)
+    del disp
+    _free()
+
+
+@pytest.mark.parametrize("xnt", [1, 2])
+def test_dispatch_x_loads_every_launch_shape(xnt):
+    """Both load forms on the multi-chunk copy (rows split into segments of
+    several chunks per lane) and the one-chunk copy."""
+    rng = np.random.default_rng(10)
+    T, E, K = 1001, 64, 8
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    ids[rng.random((T, K)) < 0.05] = -1
+    for seg in ((2, 3, 0, 16, 3), (14, 14, 0, 14, 16)):
+        _edge(T, 1003, 2048, 200, E, K, "bf16", ids, segments=seg,
+              tuning={"dispatch_x_nontemporal": xnt})
+        _edge(T, T, T, 7168, E, K, "bf16", ids, segments=seg,
+              tuning={"dispatch_x_nontemporal": xnt})
+    _edge(T, T, T, 36, E, K, "f32", ids, tuning={"dispatch_x_nontemporal": xnt})
+
+
 @pytest.mark.parametrize("burst", [1, 2])
 def test_dispatch_store_schedules_with_no_expert_slots(burst):
     rng = np.random.default_rng(8)

@@ -298,6 +298,7 @@ def test_tuning_roundtrip_and_limits(lib):
     assert t.layout_launches == -1                   # layout launches chosen by size
     assert t.dispatch_store_burst == 2               # dispatch stores paced by default
     assert t.combine_backward_store == 2             # 470 MB of dL/dy_e: ordinary stores
+    assert t.dispatch_x_nontemporal == 1             # 470 MB expert buffer: x streamed
     assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 2))) == L.MOE_OK
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.layout_launches == 2
     assert lib.moe_set_tuning(ctx, C.byref(L.MoeTuning(4, 3, 1, 1, 2, 16, 1, 1))) == L.MOE_OK
@@ -323,13 +324,24 @@ def test_tuning_roundtrip_and_limits(lib):
     for v in (3, -1):
         t.combine_backward_store = v
         assert lib.moe_set_tuning(ctx, C.byref(t)) == L.MOE_ERR_INVALID_ARG
+    t.combine_backward_store = 0
+    t.dispatch_x_nontemporal = 2
+    assert lib.moe_set_tuning(ctx, C.byref(t)) == L.MOE_OK
+    t.dispatch_x_nontemporal = 0                     # 0 keeps the current value
+    assert lib.moe_set_tuning(ctx, C.byref(t)) == L.MOE_OK
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.dispatch_x_nontemporal == 2
+    for v in (3, -1):
+        t.dispatch_x_nontemporal = v
+        assert lib.moe_set_tuning(ctx, C.byref(t)) == L.MOE_ERR_INVALID_ARG
     lib.moe_destroy(ctx)
     ctx, _, _ = _ctx(lib, _cfg(nmax=256, D=1024))    # 4 MB of dL/dy_e: cached
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_backward_store == 2
+    assert t.dispatch_x_nontemporal == 2             # 4 MB expert buffer: x cached
     lib.moe_destroy(ctx)
     ctx, _, _ = _ctx(lib, _cfg(nmax=32768))         # 470 MB output: streamed
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_store_nontemporal == 1
     assert t.combine_backward_store == 1             # 3.76 GB of dL/dy_e: streamed
+    assert t.dispatch_x_nontemporal == 2             # 3.76 GB expert buffer: x cached
     for bad in ((17, 1, 0, 0, 0, 0, 0), (-1, 1, 0, 0, 0, 0, 0), (1, 1, 0, 0, 17, 0, 0),
                 (1, 1, 0, 0, 0, -2, 0), (1, 1, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, -2),
                 (1, 1, 0, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, 0, -1)):
