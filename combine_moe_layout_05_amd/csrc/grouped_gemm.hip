@@ -44,11 +44,12 @@
 //     fragment registers: 8 wavefronts of two feature blocks (512 features
 //     per tile) share each row tile, so the rows are re-read 4x less often,
 //     and each row fragment read from LDS feeds both blocks' products.
-//     Measured on MI355X (256 experts, 7168 -> 4096, interleaved on one box,
-//     bitwise-equal outputs): 14.15-14.20 against 14.75-14.88 ms at 32768
-//     tokens, 3.33-3.34 against 3.36-3.37 ms at 4096 tokens, compared with
-//     16 wavefronts of one block; the two-block wavefront needs up to 256
-//     VGPRs, so a SIMD holds 2 of them instead of 4.
+//     Measured on MI355X (256 experts, 7168 -> 4096, interleaved on one box
+//     through the C ABI, bitwise-equal outputs): 13.98-14.13 against
+//     14.60-14.75 ms at 32768 tokens (uniform routing), 13.93-13.97 against
+//     14.32-14.38 ms (Zipf), 3.41-3.42 against 3.45 ms at 4096 tokens,
+//     compared with 16 wavefronts of one block; the two-block wavefront needs
+//     up to 256 VGPRs, so a SIMD holds 2 of them instead of 4.
 // 16-byte chunks sit in LDS at a position XOR-swizzled by the row index, so
 // fragment reads are free of bank conflicts. Loads run kStages steps ahead
 // in a register ring, weights and rows of a step issued together; the loop
