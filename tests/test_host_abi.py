@@ -342,6 +342,7 @@ def test_tuning_roundtrip_and_limits(lib):
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_store_nontemporal == 1
     assert t.combine_backward_store == 1             # 3.76 GB of dL/dy_e: streamed
     assert t.dispatch_x_nontemporal == 2             # 3.76 GB expert buffer: x cached
+    assert t.dispatch_block_waves == 4               # and 4-wavefront dispatch workgroups
     for bad in ((17, 1, 0, 0, 0, 0, 0), (-1, 1, 0, 0, 0, 0, 0), (1, 1, 0, 0, 17, 0, 0),
                 (1, 1, 0, 0, 0, -2, 0), (1, 1, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, -2),
                 (1, 1, 0, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, 0, -1)):
