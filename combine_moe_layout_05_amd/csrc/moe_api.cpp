@@ -251,6 +251,15 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     // routing), 1518.4-1529.8 against 1529.0-1535.6 us (uniform).
     if (d.max_rows * d.row_bytes > 4 * moe::kLastLevelCacheBytes && seg_eff >= 4)
         c->tuning.dispatch_block_waves = 4;
+    // Expert buffers of at most half the last-level cache: 16-wavefront
+    // dispatch workgroups (several token rows each). Measured on MI355X,
+    // steps of three runs each against one token row per workgroup: 2047
+    // tokens of 2048 bf16 with a 4096-token capacity (128 MiB) 33.2 against
+    // 35.2-35.4 us; 2048 of 4096 (128 MiB) 53.4-53.5 against 55.6-56.0;
+    // 1024 of 7168 (117 MB) equal; 8192 of 2048 (256 MiB) 108.2 against
+    // 105.1-105.5, so the rule stops at half the cache.
+    if (d.max_rows * d.row_bytes <= moe::kLastLevelCacheBytes / 2 && seg_eff >= 4)
+        c->tuning.dispatch_block_waves = moe::kMaxBlockWaves;
     c->tuning.combine_block_waves = moe::kMaxBlockWaves;
     // Stream y past the caches when the whole output buffer exceeds the
     // last-level cache: it cannot stay cached for its consumer, and ordinary

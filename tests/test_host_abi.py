@@ -337,6 +337,15 @@ def test_tuning_roundtrip_and_limits(lib):
     ctx, _, _ = _ctx(lib, _cfg(nmax=256, D=1024))    # 4 MB of dL/dy_e: cached
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_backward_store == 2
     assert t.dispatch_x_nontemporal == 2             # 4 MB expert buffer: x cached
+    assert t.dispatch_block_waves == 16              # one-chunk rows: 16-wavefront workgroups
+    lib.moe_destroy(ctx)
+    ctx, _, _ = _ctx(lib, _cfg(nmax=4096, D=2048, E=128))   # 128 MiB expert buffer, 4 KiB rows
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
+    assert (t.dispatch_segments, t.dispatch_block_waves) == (4, 16)
+    lib.moe_destroy(ctx)
+    ctx, _, _ = _ctx(lib, _cfg(nmax=8192, D=2048, E=128))   # 256 MiB: one token row
+    assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
+    assert (t.dispatch_segments, t.dispatch_block_waves) == (4, 4)
     lib.moe_destroy(ctx)
     ctx, _, _ = _ctx(lib, _cfg(nmax=32768))         # 470 MB output: streamed
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK and t.combine_store_nontemporal == 1
