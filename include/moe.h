@@ -395,9 +395,12 @@ int64_t moe_tiled_weights_bytes(int32_t num_experts, int32_t n_out, int32_t k_in
 int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t n_out,
                             int32_t k_in, void *d_tiled, void *stream);
 
-/* Launch shape tuning (optional). Each token row is split into `segments`
- * wavefront work items (1..16) and `block_waves` wavefronts (1..16) form a
- * workgroup; 0 keeps the current value. A nonzero *_nontemporal marks
+/* Launch shape tuning (optional). moe_create picks every default from the
+ * context's sizes (measured on MI355X); moe_get_tuning reports them. Each
+ * token row is split into `segments` wavefront work items (1..16) and
+ * `block_waves` wavefronts (1..16) form a workgroup (dispatch by default:
+ * one token row per workgroup; 4 wavefronts when the expert buffer exceeds
+ * 1 GiB, 16 when it is at most 128 MiB); 0 keeps the current value. A nonzero *_nontemporal marks
  * dispatch's expert-buffer stores / combine's expert-output loads / combine's
  * output stores as streaming (not kept in cache); for the last one -1 keeps
  * the current value. layout_launches 1 runs moe_layout as one launch (every
