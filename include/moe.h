@@ -400,10 +400,10 @@ int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t 
  * token row is split into `segments` wavefront work items (1..16) and
  * `block_waves` wavefronts (1..16) form a workgroup (dispatch by default:
  * one token row per workgroup; 4 wavefronts when the expert buffer exceeds
- * 1 GiB, 16 when it is at most 128 MiB); 0 keeps the current value. A nonzero *_nontemporal marks
- * dispatch's expert-buffer stores / combine's expert-output loads / combine's
- * output stores as streaming (not kept in cache); for the last one -1 keeps
- * the current value. layout_launches 1 runs moe_layout as one launch (every
+ * 1 GiB, 16 when it is at most 128 MiB); 0 keeps the current value. A
+ * nonzero *_nontemporal marks dispatch's expert-buffer stores / combine's
+ * expert-output loads / combine's output stores as streaming (not kept in
+ * cache); for the last one -1 keeps the current value. layout_launches 1 runs moe_layout as one launch (every
  * workgroup counts the whole batch, then ranks its tile), 2 as two (count,
  * then offsets and rank), -1 chooses by size (one launch up to 32768
  * slots, the default), 0 keeps the current value. dispatch_store_burst 1
