@@ -261,9 +261,19 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
                           int32_t* __restrict__ src_map) {
     constexpr int kWaves = kLayoutSingleThreads / 64;
     constexpr int64_t kTile = int64_t(kLayoutSingleThreads) * R;
-    // Per-wavefront rank counts, wavefront w at [w * kMaxExperts, ...); the
-    // count step uses the same words for its copies first.
-    __shared__ int32_t wave_hist[kWaves * kMaxExperts];
+    // Count copies: lane l adds into copy l % 8, rows 2c (slots before the
+    // tile) and 2c + 1 (the rest) of kCntStride words each, so the lanes of
+    // one instruction that share an expert (a hot expert, or the same k-slot
+    // of neighbouring tokens) mostly hit different words, and the odd stride
+    // puts an expert's word in different LDS banks across the copies. Ids
+    // outside [0, E) add into word E of the row, which is never read, so the
+    // count needs no branch per slot. The rank step then uses the same words
+    // as per-wavefront rank counts, wavefront w at [w * kMaxExperts, ...).
+    constexpr int kCopies = 8;
+    constexpr int kCntStride = kMaxExperts + 1;
+    constexpr int kCntWords = 2 * kCopies * kCntStride;
+    constexpr int kRankWords = kWaves * kMaxExperts;
+    __shared__ int32_t wave_hist[kCntWords > kRankWords ? kCntWords : kRankWords];
     __shared__ int32_t before[kMaxExperts];   // count before the tile, then the tile's first row
     __shared__ int32_t rest[kMaxExperts];     // count from the tile on
     __shared__ int32_t wave_sum[kWaves];
@@ -280,51 +290,66 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
 #pragma unroll
     for (int j = 0; j < R; ++j) ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
 
-    // Count copies: lane l adds into copy l % 8, split into the slots before
-    // the tile and the rest, so the lanes of one instruction that share an
-    // expert (a hot expert, or the same k-slot of neighbouring tokens) mostly
-    // hit different words. The copies live in wave_hist, which the rank step
-    // only needs afterwards.
-    constexpr int kCopies = 8;
-    static_assert(kCopies * 2 <= kWaves, "count copies fit in the per-wavefront histograms");
     int32_t* cnt = wave_hist;
-    int32_t* my_cnt = cnt + (lane % kCopies) * 2 * kMaxExperts;
+    int32_t* my_cnt = cnt + (lane % kCopies) * 2 * kCntStride;
     for (int e = tid; e < E; e += kLayoutSingleThreads) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) wave_hist[w * kMaxExperts + e] = 0;
+        for (int w = 0; w < 2 * kCopies; ++w) cnt[w * kCntStride + e] = 0;
     }
     __syncthreads();
 
     // Count every slot. The body is read as 16-byte quads of ids, thread tid
-    // taking quads tid, tid + 1024, ..., eight loads in flight before their
-    // adds; the slots before the first 16-byte boundary and after the last
-    // whole quad are read one by one. Ids outside [0, E) count nowhere.
+    // taking quads tid, tid + 1024, ..., eight loads in flight (addresses
+    // clamped into the batch) before their adds; only whole quads past the
+    // batch are skipped. With 16-byte aligned ids a quad lies on one side of
+    // the tile start, so its row is chosen once. The slots before the first
+    // 16-byte boundary and after the last whole quad are read one by one.
     {
         auto add = [&](int32_t e, int64_t i) {
             if (static_cast<uint32_t>(e) < static_cast<uint32_t>(E))
-                atomicAdd(&my_cnt[(i < tile0 ? 0 : kMaxExperts) + e], 1);
+                atomicAdd(&my_cnt[(i < tile0 ? 0 : kCntStride) + e], 1);
         };
         const int64_t mis = static_cast<int64_t>((reinterpret_cast<uintptr_t>(ids) >> 2) & 3);
         const int64_t head = mis == 0 ? 0 : (4 - mis < nvalid ? 4 - mis : nvalid);
-        const int64_t nq = (nvalid - head) / 4;
-        const int64_t tail0 = head + 4 * nq;
+        const int32_t nq = static_cast<int32_t>((nvalid - head) / 4);
+        const int64_t tail0 = head + 4 * int64_t(nq);
         if (tid < head) add(ids[tid], tid);
         if (tail0 + tid < nvalid) add(ids[tail0 + tid], tail0 + tid);
         const v4i* quads = reinterpret_cast<const v4i*>(ids + head);
+        const uint32_t uE = static_cast<uint32_t>(E);
+        const int64_t tq = tile0 - head;  // the tile start, in slots from the first quad
         constexpr int kU = 8;
-        constexpr int64_t kStep = kLayoutSingleThreads;
-        for (int64_t j0 = tid; j0 < nq; j0 += kU * kStep) {
+        constexpr int kStep = kLayoutSingleThreads;
+        for (int32_t j0 = tid; j0 < nq; j0 += kU * kStep) {
             v4i v[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const int64_t j = j0 + u * kStep;
-                v[u] = j < nq ? quads[j] : v4i{-1, -1, -1, -1};
+                const int32_t j = j0 + u * kStep;
+                v[u] = quads[j < nq ? j : nq - 1];
             }
+            if (head == 0) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int64_t i = head + 4 * (j0 + u * kStep);
+                for (int u = 0; u < kU; ++u) {
+                    const int32_t j = j0 + u * kStep;
+                    int32_t* row = my_cnt + (4 * int64_t(j) < tq ? 0 : kCntStride);
+                    if (j < nq) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) add(v[u][c], i + c);
+                        for (int c = 0; c < 4; ++c)
+                            atomicAdd(&row[min(static_cast<uint32_t>(v[u][c]), uE)], 1);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int32_t j = j0 + u * kStep;
+                    if (j < nq) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            int32_t* row = my_cnt + (4 * int64_t(j) + c < tq ? 0 : kCntStride);
+                            atomicAdd(&row[min(static_cast<uint32_t>(v[u][c]), uE)], 1);
+                        }
+                    }
+                }
             }
         }
     }
@@ -333,8 +358,8 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
         int32_t b = 0, r = 0;
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) {
-            b += cnt[(2 * c) * kMaxExperts + e];
-            r += cnt[(2 * c + 1) * kMaxExperts + e];
+            b += cnt[(2 * c) * kCntStride + e];
+            r += cnt[(2 * c + 1) * kCntStride + e];
         }
         before[e] = b;
         rest[e] = r;
