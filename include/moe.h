@@ -218,7 +218,9 @@ int moe_dispatch(moe_ctx *ctx, const void *d_x, const float *d_topk_scores,
  * 2 and 3: the counts and the total stay on the device). The count launch's
  * last workgroup to finish scans the per-tile expert histograms into each
  * tile's first row per expert; the dispatch workgroups rank their tokens'
- * slots within their tile, record the rows and copy the hidden states. No
+ * slots within their tile, record the rows and copy the hidden states. Each
+ * dispatch workgroup holds one whole token row when a row spans at least 4
+ * wavefronts, unless moe_set_tuning set dispatch_block_waves. No
  * workgroup waits on another. The last workgroup is found with a completion
  * counter that lives in a static device array (one slot per context, taken
  * at moe_create and given back at moe_destroy; MOE_ERR_UNSUPPORTED when all
