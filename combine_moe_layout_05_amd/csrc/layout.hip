@@ -52,12 +52,20 @@ __device__ __forceinline__ uint64_t peer_mask(int32_t key, bool valid, int bits)
     return m;
 }
 
-// Expert of slot i, or -1 for padding slots and ids outside [0,E).
-__device__ __forceinline__ int32_t slot_expert(const int32_t* __restrict__ ids,
-                                               int64_t i, int64_t nvalid, int32_t E) {
-    if (i >= nvalid) return -1;
-    const int32_t e = ids[i];
-    return (static_cast<uint32_t>(e) < static_cast<uint32_t>(E)) ? e : -1;
+// The id of slot i, loaded without a branch (the index is clamped into the
+// batch), so the load's wait comes at the value's first use rather than
+// right after it; slot_expert_of then discards padding slots. No load at all
+// for an empty batch, whose id array may be absent.
+__device__ __forceinline__ int32_t load_slot_id(const int32_t* __restrict__ ids, int64_t i,
+                                                int64_t nvalid) {
+    if (nvalid <= 0) return -1;
+    return ids[i < nvalid ? i : nvalid - 1];
+}
+
+// Expert of slot i given its loaded id, or -1 for padding slots and ids
+// outside [0,E).
+__device__ __forceinline__ int32_t slot_expert_of(int32_t id, int64_t i, int64_t nvalid, int32_t E) {
+    return (i < nvalid && static_cast<uint32_t>(id) < static_cast<uint32_t>(E)) ? id : -1;
 }
 
 // Histogram rows are padded to E4 = round_up(E, 4) entries (zeros past E) so
@@ -76,8 +84,9 @@ void layout_count_kernel(const int32_t* __restrict__ ids, int64_t nvalid,
     const int64_t base = int64_t(blockIdx.x) * (kLayoutThreads * R) + wave * (64 * R);
     int32_t ex[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-        ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
+    for (int j = 0; j < R; ++j) ex[j] = load_slot_id(ids, base + j * 64 + lane, nvalid);
+#pragma unroll
+    for (int j = 0; j < R; ++j) ex[j] = slot_expert_of(ex[j], base + j * 64 + lane, nvalid, E);
 
     const uint64_t below = lanes_below();
 #pragma unroll
@@ -113,6 +122,12 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int32_t blk = static_cast<int32_t>(blockIdx.x);
+    // This wavefront's slots, loaded first so that the load overlaps the
+    // tile sums below: slots base + j*64 + lane.
+    const int64_t base = int64_t(blockIdx.x) * (kLayoutThreads * R) + wave * (64 * R);
+    int32_t ex[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) ex[j] = load_slot_id(ids, base + j * 64 + lane, nvalid);
 
     // Per expert: the total over all tiles and the part in tiles before this
     // one. Thread (quad q, slice sl) sums experts 4q..4q+3 over tiles
@@ -190,12 +205,9 @@ void layout_rank_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64_t
         offsets[E] = total;
     }
 
-    const int64_t base = int64_t(blockIdx.x) * (kLayoutThreads * R) + wave * (64 * R);
-    int32_t ex[R];
     int32_t local[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-        ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
+    for (int j = 0; j < R; ++j) ex[j] = slot_expert_of(ex[j], base + j * 64 + lane, nvalid, E);
 
     // Rank within this wavefront's run, chunk by chunk in slot order. All
     // peers read the expert's running count before the lowest peer advances
@@ -288,7 +300,7 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
     const int64_t base = tile0 + wave * (64 * R);
     int32_t ex[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
+    for (int j = 0; j < R; ++j) ex[j] = load_slot_id(ids, base + j * 64 + lane, nvalid);
 
     int32_t* cnt = wave_hist;
     int32_t* my_cnt = cnt + (lane % kCopies) * 2 * kCntStride;
@@ -394,6 +406,8 @@ void layout_single_kernel(const int32_t* __restrict__ ids, int64_t nvalid, int64
     if (blockIdx.x == 0 && tid == kLayoutSingleThreads - 1) offsets[E] = run + mine_tot;
 
     // Rank this tile's slots (loaded into ex[] above).
+#pragma unroll
+    for (int j = 0; j < R; ++j) ex[j] = slot_expert_of(ex[j], base + j * 64 + lane, nvalid, E);
     int32_t local[R];
     int32_t* mine = wave_hist + wave * kMaxExperts;
     const uint64_t below = lanes_below();
@@ -472,7 +486,9 @@ void layout_count_scan_kernel(const int32_t* __restrict__ ids, int64_t nvalid, i
         const int64_t base = int64_t(blockIdx.x) * kTile + wave * (64 * R);
         int32_t ex[R];
 #pragma unroll
-        for (int j = 0; j < R; ++j) ex[j] = slot_expert(ids, base + j * 64 + lane, nvalid, E);
+        for (int j = 0; j < R; ++j) ex[j] = load_slot_id(ids, base + j * 64 + lane, nvalid);
+#pragma unroll
+        for (int j = 0; j < R; ++j) ex[j] = slot_expert_of(ex[j], base + j * 64 + lane, nvalid, E);
         const uint64_t below = lanes_below();
 #pragma unroll
         for (int j = 0; j < R; ++j) {
