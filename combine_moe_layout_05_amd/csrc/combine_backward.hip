@@ -79,10 +79,12 @@ void combine_backward_kernel(const v4i* __restrict__ grad_y, const v4i* __restri
     }
 
     if (tid < K) {
+        // Both loads are issued before either is used.
         const int32_t r = row_map[t * K + tid];
+        const float sv = scores[t * K + tid];
         const bool ok = r >= 0 && r < row_limit;
         tok_rows[tid] = ok ? r : -1;
-        tok_scores[tid] = ok ? scores[t * K + tid] : 0.0f;
+        tok_scores[tid] = ok ? sv : 0.0f;
     }
     __syncthreads();
     int32_t row[K];
