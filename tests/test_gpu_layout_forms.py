@@ -110,3 +110,33 @@ def test_layout_forms_alternate_on_one_context():
         assert np.array_equal(g["src"], ref[key]["src"])
         assert np.array_equal(g["offsets"], ref[key]["offsets"])
     del disp
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+@pytest.mark.parametrize("shape", [(4096, 4096, 256, 8), (1001, 1003, 3, 3), (5, 8, 16, 2)],
+                         ids=["dsv3", "ragged_K3", "tiny_T5"])
+def test_layout_forms_ids_off_16_byte_alignment(shift, shape):
+    """Ids whose device address is 4, 8 or 12 bytes past a 16-byte boundary (a
+    view into a larger buffer): the one-launch count reads the slots before
+    the first boundary and after the last whole quad one by one, and decides
+    per slot which side of the tile start each falls on."""
+    T, ntpr, E, K = shape
+    ids = _ids(T, E, K, "zipf" if E > 8 else "uniform", 1.1, 30 + shift, bad=True)
+    buf = torch.full((T * K + 8,), -1, dtype=torch.int32, device=DEV)
+    view = buf[shift:shift + T * K].view(T, K)
+    view.copy_(i32_dev(ids))
+    assert view.data_ptr() % 16 == 4 * shift
+    disp = MoeDispatcher(ntpr + 1, 64, E, K, dtype=torch.bfloat16, device=DEV)
+    o = oracle.layout(ids, T, ntpr, E, K)
+    for launches in (1, 2):
+        note(f"layout form {launches}: ids shifted by {4 * shift} bytes, T={T} E={E} K={K}")
+        disp.set_tuning(layout_launches=launches)
+        lay = disp.layout(view, ntpr)
+        sync_or_fail()
+        total = int(lay.offsets[-1].item())
+        assert total == o["total"]
+        assert np.array_equal(lay.counts.cpu().numpy(), o["counts"])
+        assert np.array_equal(lay.offsets.cpu().numpy(), o["offsets"])
+        assert np.array_equal(lay.row_map.cpu().numpy().reshape(-1), o["row_map"].reshape(-1))
+        assert np.array_equal(disp.src_map[:total].cpu().numpy(), o["src"])
+    del disp
