@@ -45,6 +45,13 @@ namespace {
 
 constexpr int64_t kAlign = MOE_WORKSPACE_ALIGN;
 
+// Whether device address p is not a multiple of a (a power of two). Hidden
+// state rows are read and written as 16-byte vectors; int32 and float32
+// arrays are read element by element or as vectors of their own type.
+bool misaligned(const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+
 int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t elem_bytes(int32_t dtype) {
@@ -392,7 +399,7 @@ int moe_layout(moe_ctx* ctx, const int32_t* d_topk_ids, int32_t T, int32_t ntpr,
     int64_t ntpr4 = 0;
     const int st = check_call(ctx, T, ntpr, &ntpr4);
     if (st != MOE_OK) return st;
-    if (T > 0 && !d_topk_ids) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!d_topk_ids || misaligned(d_topk_ids, 4))) return MOE_ERR_INVALID_ARG;
     if (moe::launch_layout(layout_args(ctx, d_topk_ids, T, ntpr4),
                            static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
@@ -410,7 +417,10 @@ int moe_layout_noalloc(const int32_t* d_topk_ids, int32_t T, int32_t ntpr, int32
     const int64_t nslots = moe_round_up4(ntpr) * K;
     if (nslots > int64_t(INT32_MAX) - moe::kLayoutTile) return MOE_ERR_INVALID_ARG;
     if (!d_counts || !d_offsets || !d_row_map || !d_src_map) return MOE_ERR_INVALID_ARG;
-    if (T > 0 && !d_topk_ids) return MOE_ERR_INVALID_ARG;
+    if (misaligned(d_counts, 4) || misaligned(d_offsets, 4) || misaligned(d_row_map, 4) ||
+        misaligned(d_src_map, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!d_topk_ids || misaligned(d_topk_ids, 4))) return MOE_ERR_INVALID_ARG;
     static_assert(MOE_NOALLOC_SCRATCH_BYTES == moe::kNoallocScratchBytes, "one scratch size");
     moe::LayoutArgs a;
     a.ids = d_topk_ids;
@@ -440,6 +450,8 @@ static int dispatch_impl(moe_ctx* ctx, const void* d_x, const float* d_scores,
     if (st != MOE_OK) return st;
     if (d_counts != at<int32_t>(ctx, ctx->desc.counts)) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!d_x || !d_scores || !d_ids)) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (misaligned(d_x, 16) || misaligned(d_scores, 4) || misaligned(d_ids, 4)))
+        return MOE_ERR_INVALID_ARG;
     if (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4)
         return MOE_ERR_STATE;
     if (moe::launch_dispatch(dispatch_args(ctx, d_x, d_scores, T, scaled),
@@ -456,6 +468,8 @@ int moe_layout_dispatch(moe_ctx* ctx, const void* d_x, const float* d_scores,
     if (st != MOE_OK) return st;
     if (ctx->counter_slot < 0) return MOE_ERR_UNSUPPORTED;
     if (T > 0 && (!d_x || !d_scores || !d_topk_ids)) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (misaligned(d_x, 16) || misaligned(d_scores, 4) || misaligned(d_topk_ids, 4)))
+        return MOE_ERR_INVALID_ARG;
     moe::FusedLayoutDispatchArgs a;
     a.layout = layout_args(ctx, d_topk_ids, T, ntpr4);
     a.dispatch = dispatch_args(ctx, d_x, d_scores, T, false);
@@ -499,7 +513,7 @@ int moe_topk_from_routing_map(moe_ctx* ctx, const uint8_t* d_routing_map, const 
     if (!ctx || !d_topk_ids_out || !d_topk_scores_out || !d_n_experts_out)
         return MOE_ERR_INVALID_ARG;
     if (T < 0 || T > ctx->cfg.num_max_tokens_per_rank) return MOE_ERR_CAPACITY;
-    if (T > 0 && (!d_routing_map || !d_probs)) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!d_routing_map || !d_probs || misaligned(d_probs, 4))) return MOE_ERR_INVALID_ARG;
     moe::TopkFromMapArgs a;
     a.map = d_routing_map;
     a.probs = d_probs;
@@ -526,6 +540,9 @@ int moe_combine(moe_ctx* ctx, const void* d_y_expert, const int32_t* d_row_map,
     // d_scores may be NULL: every weight is then 1 (the scores were applied
     // by moe_dispatch_scaled, or the caller wants the plain sum).
     if (T > 0 && (!d_y_expert || !d_row_map)) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (misaligned(d_y_expert, 16) || misaligned(d_row_map, 4) ||
+                  (d_scores && misaligned(d_scores, 4))))
+        return MOE_ERR_INVALID_ARG;
     if (d_row_map == at<int32_t>(ctx, ctx->desc.row_map) &&
         (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4))
         return MOE_ERR_STATE;
@@ -559,6 +576,10 @@ int moe_combine_backward(moe_ctx* ctx, const void* d_grad_y, const void* d_y_exp
     const int st = check_call(ctx, T, ntpr, &ntpr4);
     if (st != MOE_OK) return st;
     if (T > 0 && (!d_grad_y || !d_y_expert || !d_row_map || !d_scores)) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (misaligned(d_grad_y, 16) || misaligned(d_y_expert, 16) ||
+                  misaligned(d_row_map, 4) || misaligned(d_scores, 4)))
+        return MOE_ERR_INVALID_ARG;
+    if (d_total && misaligned(d_total, 4)) return MOE_ERR_INVALID_ARG;
     if (d_row_map == at<int32_t>(ctx, ctx->desc.row_map) &&
         (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4))
         return MOE_ERR_STATE;
@@ -591,6 +612,8 @@ int moe_dispatch_backward(moe_ctx* ctx, const void* d_grad_x_expert, const int32
     const int st = check_call(ctx, T, ntpr, &ntpr4);
     if (st != MOE_OK) return st;
     if (T > 0 && (!d_grad_x_expert || !d_row_map)) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (misaligned(d_grad_x_expert, 16) || misaligned(d_row_map, 4)))
+        return MOE_ERR_INVALID_ARG;
     if (d_row_map == at<int32_t>(ctx, ctx->desc.row_map) &&
         (!ctx->has_layout || ctx->layout_T != T || ctx->layout_ntpr4 != ntpr4))
         return MOE_ERR_STATE;
@@ -619,10 +642,6 @@ int moe_dispatch_backward(moe_ctx* ctx, const void* d_grad_x_expert, const int32
 static bool gemm_sizes_ok(int32_t num_experts, int32_t n_out, int32_t k_in) {
     return num_experts >= 1 && num_experts <= MOE_MAX_EXPERTS && k_in >= 8 && k_in % 8 == 0 &&
            n_out >= 8 && n_out % 8 == 0;
-}
-
-static bool misaligned(const void* p, uintptr_t a) {
-    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
 }
 
 int moe_grouped_gemm(const void* d_x_expert, const void* d_weights, const int32_t* d_offsets,

@@ -27,6 +27,10 @@
  *     scores float32, hidden states fp32 or bf16 (config dtype).
  *   - Matrices are row-major and contiguous: ids and scores [T][K], hidden
  *     states [T][hidden].
+ *   - Device pointers to hidden-state rows (x, expert outputs and their
+ *     gradients) must be 16-byte aligned, int32 and float32 arrays 4-byte
+ *     aligned (every torch allocation is; a view that starts at an element
+ *     offset may not be): MOE_ERR_INVALID_ARG otherwise.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued on it asynchronously; no call synchronizes,
  *     allocates device memory, sets memory or copies device-to-host, so the

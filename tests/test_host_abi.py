@@ -163,6 +163,19 @@ def test_calls_reject_bad_arguments_before_enqueueing(lib):
     assert lib.moe_combine(ctx, None, row_map, s, 5, 8, None, C.byref(out)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctx, base + d.x_e, row_map, s, 5, 8, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctx, base + d.x_e, row_map, s, 9, 8, None, C.byref(out)) == L.MOE_ERR_CAPACITY
+    # alignment: 16 bytes for hidden-state rows, 4 for int32 / float32 arrays
+    assert lib.moe_layout(ctx, ids + 2, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctx, x + 8, s, ids, counts, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctx, x, s + 2, ids, counts, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctx, x, s, ids + 1, counts, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctx, base + d.x_e + 4, row_map, s, 5, 8, None,
+                           C.byref(out)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctx, base + d.x_e, row_map + 2, s, 5, 8, None,
+                           C.byref(out)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctx, base + d.x_e, row_map, s + 1, 5, 8, None,
+                           C.byref(out)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_layout_dispatch(ctx, x + 8, s, ids, 5, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_layout_dispatch(ctx, x, s, ids + 2, 5, 8, None) == L.MOE_ERR_INVALID_ARG
     lib.moe_destroy(ctx)
 
 
@@ -187,6 +200,13 @@ def test_backward_calls_need_the_flag_and_a_matching_layout(lib):
                                     C.byref(out_s)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(ctx, None, p, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_backward(ctx, p, p, 5, 4097, None, C.byref(out_x)) == L.MOE_ERR_CAPACITY
+    # alignment (checked before the layout state)
+    for args in [(p + 8, p, rm, p, p), (p, p + 8, rm, p, p), (p, p, rm + 2, p, p),
+                 (p, p, rm, p + 2, p), (p, p, rm, p, p + 1)]:
+        assert lib.moe_combine_backward(ctx, *args, 5, 8, None, C.byref(out_e),
+                                        C.byref(out_s)) == L.MOE_ERR_INVALID_ARG, args
+    assert lib.moe_dispatch_backward(ctx, p + 4, rm, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_backward(ctx, p, rm + 2, 5, 8, None, C.byref(out_x)) == L.MOE_ERR_INVALID_ARG
     lib.moe_destroy(ctx)
 
 
@@ -394,6 +414,12 @@ def test_layout_noalloc_rejects_bad_arguments_before_any_launch(lib):
         outs[i] = None
         assert f(p, 5, 8, 16, 2, *outs, None) == L.MOE_ERR_INVALID_ARG
     assert f(p, 0, (2**31 - 512) // 16 + 4, 16, 16, p, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    odd = (1 << 40) + 2                                                      # not 4-byte aligned
+    assert f(odd, 5, 8, 16, 2, p, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    for i in range(4):
+        outs = [p, p, p, p]
+        outs[i] = odd
+        assert f(p, 5, 8, 16, 2, *outs, None) == L.MOE_ERR_INVALID_ARG
     # Scratch: 1024-slot tiles above 65536 slots, one row of round_up4(E)
     # int32 per tile, 4 MiB in all.
     assert L.MOE_NOALLOC_SCRATCH_BYTES == 4 << 20
