@@ -440,3 +440,31 @@ def test_call_order_and_counts_are_enforced():
     sync_or_fail()
     o = oracle.run_pipeline(b["x"], b["ids"], b["scores"], 60, 64, w.E, w.K)
     assert np.array_equal(x_to_np(y), o["y"])
+
+
+def test_misaligned_rows_are_rejected_and_nothing_runs():
+    """Hidden-state rows move as 16-byte vectors: x or expert outputs that start
+    at an element offset (a view into a larger buffer) are refused before any
+    launch, and the context's previous results stay as they were."""
+    w = workloads.WORKLOADS["padded"]
+    b = workloads.make_batch(w)
+    T = 614
+    disp = _dispatcher(w)
+    ids_d, s_d, x_d = i32_dev(b["ids"][:T]), f32_dev(b["scores"][:T]), x_to_dev(b["x"][:T])
+    lay = disp.layout(ids_d, w.ntpr)
+    disp.dispatch(x_d, s_d, ids_d, lay.counts, num_tokens_per_rank=w.ntpr)
+    y = disp.combine(disp.x_e, lay.row_map, s_d, num_tokens_per_rank=w.ntpr)
+    sync_or_fail()
+    x_e_before, y_before = disp.x_e.clone(), y.clone()
+    big = torch.empty((T * w.D + 8,), dtype=x_d.dtype, device=DEV)
+    x_off = big[1:1 + T * w.D].view(T, w.D)          # 2 bytes past a 16-byte boundary
+    x_off.copy_(x_d)
+    with pytest.raises(MoeError):
+        disp.dispatch(x_off, s_d, ids_d, lay.counts, num_tokens_per_rank=w.ntpr)
+    rows = disp.x_e.shape[0]
+    ye = torch.empty((rows * w.D + 8,), dtype=x_d.dtype, device=DEV)[4:4 + rows * w.D].view(rows, w.D)
+    with pytest.raises(MoeError):
+        disp.combine(ye, lay.row_map, s_d, num_tokens_per_rank=w.ntpr)
+    sync_or_fail()
+    assert torch.equal(disp.x_e, x_e_before)
+    assert torch.equal(y, y_before)
