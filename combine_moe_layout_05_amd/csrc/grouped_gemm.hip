@@ -14,8 +14,8 @@
 // expert, tiles go in
 // blocks of up to 8 row tiles: all feature tiles of a block, each with the
 // block's row tiles fastest. Workgroups are dealt to the 8 XCDs round-robin,
-// so tile numbers are handed out in chunks of consecutive tiles (32, or 16
-// for long segments), XCD x taking every eighth chunk (the kernel can also
+// so tile numbers are handed out in chunks of 32 consecutive tiles, XCD x
+// taking every eighth chunk (the kernel can also
 // give each XCD one contiguous run); the workgroups an XCD runs at once then
 // cover a few row tiles x feature tiles of one expert,
 // which share each weight tile and each row tile through that XCD's L2 (with

@@ -211,14 +211,17 @@ hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 // per XCD; c > 0 = chunks of c consecutive tiles dealt round-robin. Dealt in
 // chunks, each XCD gets a share of every large expert instead of a few whole
 // experts, which evens out the HBM traffic the XCDs draw, while a chunk still
-// keeps a block of one expert's tiles together in one L2. Measured on MI355X
-// (256 experts, 7168 -> 4096, each box interleaved): long segments (at least
-// 512 rows per expert at full capacity; 32768 tokens) 14.5 ms with chunks of
-// 16 against 15.2 with runs, 32 within 0.5 % of 16 either way, 64 slower;
-// shorter segments (4096 tokens) 3.46-3.49 ms with chunks of 32 against
-// 3.54-3.56 with runs, 3.51 with 16, 3.59 with 64.
+// keeps a block of one expert's tiles together in one L2. Chunks of 32 tiles
+// at every size. Measured on MI355X (256 experts, 7168 -> 4096, interleaved
+// on one box): 4096 tokens 3.46-3.49 ms with chunks of 32 against 3.54-3.56
+// with runs, 3.51 with 16, 3.59 with 64; 32768 tokens 13.91-14.08 against
+// 14.01-14.21 ms with 16 (uniform routing) and 13.90-13.97 against
+// 14.08-14.13 ms (Zipf), with about a tenth less L2-miss traffic (each row
+// tile is fetched by fewer chunks); runs there 14.9-15.2 ms.
 inline int32_t gemm_xcd_chunk(int64_t max_rows, int32_t E) {
-    return max_rows >= int64_t(512) * E ? 16 : 32;
+    (void)max_rows;
+    (void)E;
+    return 32;
 }
 inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile,
                                  int32_t features) {
