@@ -275,7 +275,16 @@ int moe_create(const moe_config* cfg, void* d_workspace, size_t bytes, moe_ctx**
     // Stream y past the caches when the whole output buffer exceeds the
     // last-level cache: it cannot stay cached for its consumer, and ordinary
     // stores would leave dirty lines to be written back during later kernels.
-    c->tuning.combine_store_nontemporal = d.nmax4 * d.row_bytes > moe::kLastLevelCacheBytes ? 1 : 0;
+    const bool y_streamed = d.nmax4 * d.row_bytes > moe::kLastLevelCacheBytes;
+    c->tuning.combine_store_nontemporal = y_streamed ? 1 : 0;
+    // With y streamed, one token row per combine workgroup. Measured on
+    // MI355X, three interleaved runs each: 32768 tokens of 7168 bf16, combine
+    // 702.2-702.5 against 717.1-717.9 us (Zipf routing) and 713.5-713.7
+    // against 725.4-726.6 us (uniform), dispatch backward 726-728 against
+    // 734-740 us; with y cached, 16 wavefronts stay ahead (4096 tokens of 7168:
+    // 96.1-96.6 against 97.5-97.9 us; 8192 of 4096: 111.4-111.7 against
+    // 115.3-115.5 us with one row of 8 wavefronts).
+    if (y_streamed && seg_eff >= 4) c->tuning.combine_block_waves = seg_eff;
     // The layout runs as one launch up to kLayoutSingleMaxSlots slots, as
     // two above (measured on MI355X).
     c->tuning.layout_launches = -1;

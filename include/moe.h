@@ -406,7 +406,9 @@ int moe_tile_expert_weights(const void *d_weights, int32_t num_experts, int32_t 
  * token row is split into `segments` wavefront work items (1..16) and
  * `block_waves` wavefronts (1..16) form a workgroup (dispatch by default:
  * one token row per workgroup; 4 wavefronts when the expert buffer exceeds
- * 1 GiB, 16 when it is at most 128 MiB); 0 keeps the current value. A
+ * 1 GiB, 16 when it is at most 128 MiB; combine by default: 16 wavefronts,
+ * one token row when the output y exceeds the last-level cache); 0 keeps the
+ * current value. A
  * nonzero *_nontemporal marks dispatch's expert-buffer stores / combine's
  * expert-output loads / combine's output stores as streaming (not kept in
  * cache); for the last one -1 keeps the current value. layout_launches 1 runs moe_layout as one launch (every

@@ -362,6 +362,7 @@ def test_tuning_roundtrip_and_limits(lib):
     ctx, _, _ = _ctx(lib, _cfg(nmax=4096, D=2048, E=128))   # 128 MiB expert buffer, 4 KiB rows
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
     assert (t.dispatch_segments, t.dispatch_block_waves) == (4, 16)
+    assert t.combine_block_waves == 16               # y cached: 16-wavefront combine workgroups
     lib.moe_destroy(ctx)
     ctx, _, _ = _ctx(lib, _cfg(nmax=8192, D=2048, E=128))   # 256 MiB: one token row
     assert lib.moe_get_tuning(ctx, C.byref(t)) == L.MOE_OK
@@ -372,6 +373,7 @@ def test_tuning_roundtrip_and_limits(lib):
     assert t.combine_backward_store == 1             # 3.76 GB of dL/dy_e: streamed
     assert t.dispatch_x_nontemporal == 2             # 3.76 GB expert buffer: x cached
     assert t.dispatch_block_waves == 4               # and 4-wavefront dispatch workgroups
+    assert t.combine_block_waves == 14               # y streamed: a combine workgroup per row
     for bad in ((17, 1, 0, 0, 0, 0, 0), (-1, 1, 0, 0, 0, 0, 0), (1, 1, 0, 0, 17, 0, 0),
                 (1, 1, 0, 0, 0, -2, 0), (1, 1, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, -2),
                 (1, 1, 0, 0, 0, 0, 0, 0, 3), (1, 1, 0, 0, 0, 0, 0, 0, -1)):
