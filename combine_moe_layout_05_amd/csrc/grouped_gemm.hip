@@ -14,10 +14,9 @@
 // expert, tiles go in
 // blocks of up to 8 row tiles: all feature tiles of a block, each with the
 // block's row tiles fastest. Workgroups are dealt to the 8 XCDs round-robin,
-// so tile numbers are handed out in chunks of 32 consecutive tiles, XCD x
-// taking every eighth chunk (the kernel can also
-// give each XCD one contiguous run); the workgroups an XCD runs at once then
-// cover a few row tiles x feature tiles of one expert,
+// so tile numbers are handed out in chunks of kGemmXcdChunk (32) consecutive
+// tiles, XCD x taking every eighth chunk; the workgroups an XCD runs at once
+// then cover a few row tiles x feature tiles of one expert,
 // which share each weight tile and each row tile through that XCD's L2 (with
 // a plain feature-major order a large expert re-fetches its rows once per
 // feature tile). The grid covers the most tiles any routing can need,
@@ -92,7 +91,7 @@ template <int BT, int WAVES, int FB, bool TILED>
 __global__ __launch_bounds__(WAVES * 64)
 void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
                          const int32_t* __restrict__ offsets, int32_t E, int32_t max_rows,
-                         int32_t chunks, int32_t N, int32_t ftiles, int32_t xcd_chunk,
+                         int32_t chunks, int32_t N, int32_t ftiles,
                          uint8_t* __restrict__ out) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kFeatures = WAVES * 32 * FB;
@@ -124,21 +123,14 @@ void grouped_gemm_kernel(const v4i* __restrict__ x_e, const v4i* __restrict__ w,
             const int64_t v = __shfl_up(incl, d, 64);
             if (lane >= d) incl += v;
         }
-        // Workgroup b runs on XCD b % kXcds (round-robin dispatch); XCD x
-        // takes the tile run [x * run, (x + 1) * run).
         const int64_t total = __shfl(incl, 63, 64);
-        // Contiguous runs: XCD x takes [x * run, (x + 1) * run). Chunks: XCD x
-        // takes chunks x, x + 8, x + 16, ... of xcd_chunk tiles each (the grid
-        // holds whole chunks per XCD, so every tile number is dealt).
+        // Workgroup b runs on XCD b % kXcds (round-robin dispatch). XCD x
+        // takes chunks x, x + 8, x + 16, ... of kGemmXcdChunk tiles each (the
+        // grid holds whole chunks per XCD, so every tile number is dealt).
         const int64_t idx = blockIdx.x / kXcds;
         const int64_t x = blockIdx.x % kXcds;
-        int64_t u;
-        if (xcd_chunk > 0) {
-            u = ((idx / xcd_chunk) * kXcds + x) * xcd_chunk + idx % xcd_chunk;
-        } else {
-            const int64_t run = (total + kXcds - 1) / kXcds;
-            u = idx < run ? x * run + idx : total;
-        }
+        const int64_t u =
+            ((idx / kGemmXcdChunk) * kXcds + x) * kGemmXcdChunk + idx % kGemmXcdChunk;
         if (lane == 0 && u >= total) info[0] = -1;
         int64_t base = incl - local;
         if (u >= base && u < incl) {
@@ -429,7 +421,7 @@ hipError_t launch_bt(const GroupedGemmArgs& a, hipStream_t stream) {
                        static_cast<const v4i*>(a.w), a.offsets, a.E,
                        static_cast<int32_t>(a.max_rows), a.Kd / 8, a.N,
                        static_cast<int32_t>((a.N + kFeatures - 1) / kFeatures),
-                       gemm_xcd_chunk(a.max_rows, a.E), static_cast<uint8_t*>(a.out));
+                       static_cast<uint8_t*>(a.out));
     return hipGetLastError();
 }
 

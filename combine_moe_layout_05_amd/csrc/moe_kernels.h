@@ -206,29 +206,25 @@ hipError_t launch_topk_from_map(const TopkFromMapArgs& a, hipStream_t stream);
 // Expert step (grouped GEMM): workgroups of the launch for max_rows rows,
 // E experts, N output features, row tiles of row_tile rows and feature tiles
 // of `features`: every (feature tile, row tile) pair the worst routing can
-// need, rounded up to a multiple of 8 (one run of tiles per XCD).
-// How tiles are dealt to the 8 XCDs: 0 = one contiguous run of tile numbers
-// per XCD; c > 0 = chunks of c consecutive tiles dealt round-robin. Dealt in
-// chunks, each XCD gets a share of every large expert instead of a few whole
-// experts, which evens out the HBM traffic the XCDs draw, while a chunk still
-// keeps a block of one expert's tiles together in one L2. Chunks of 32 tiles
-// at every size. Measured on MI355X (256 experts, 7168 -> 4096, interleaved
-// on one box): 4096 tokens 3.46-3.49 ms with chunks of 32 against 3.54-3.56
-// with runs, 3.51 with 16, 3.59 with 64; 32768 tokens 13.91-14.08 against
-// 14.01-14.21 ms with 16 (uniform routing) and 13.90-13.97 against
-// 14.08-14.13 ms (Zipf), with about a tenth less L2-miss traffic (each row
-// tile is fetched by fewer chunks); runs there 14.9-15.2 ms.
-inline int32_t gemm_xcd_chunk(int64_t max_rows, int32_t E) {
-    (void)max_rows;
-    (void)E;
-    return 32;
-}
+// need, rounded up to whole chunks of tiles per XCD.
+// Tile numbers are dealt to the 8 XCDs in chunks of kGemmXcdChunk
+// consecutive tiles, round-robin. Each XCD then gets a share of every large
+// expert instead of a few whole experts, which evens out the HBM traffic the
+// XCDs draw, while a chunk still keeps a block of one expert's tiles together
+// in one L2. Measured on MI355X (256 experts, 7168 -> 4096, interleaved on
+// one box): 4096 tokens 3.46-3.49 ms with chunks of 32 against 3.54-3.56
+// with one contiguous run of tile numbers per XCD, 3.51 with chunks of 16,
+// 3.59 with 64; 32768 tokens 13.91-14.08 against 14.01-14.21 ms with 16
+// (uniform routing) and 13.90-13.97 against 14.08-14.13 ms (Zipf), with
+// about a tenth less L2-miss traffic (each row tile is fetched by fewer
+// chunks); contiguous runs there 14.9-15.2 ms.
+constexpr int32_t kGemmXcdChunk = 32;
 inline int64_t grouped_gemm_grid(int64_t max_rows, int32_t E, int32_t N, int32_t row_tile,
                                  int32_t features) {
     const int64_t ftiles = (int64_t(N) + features - 1) / features;
     const int64_t tiles = ftiles * ((max_rows + row_tile - 1) / row_tile + E);
     // Whole chunks per XCD, so the dealt tile numbers cover [0, grid).
-    const int64_t unit = 8 * int64_t(gemm_xcd_chunk(max_rows, E) > 0 ? gemm_xcd_chunk(max_rows, E) : 1);
+    const int64_t unit = 8 * int64_t(kGemmXcdChunk);
     return (tiles + unit - 1) / unit * unit;
 }
 constexpr int kGemmRowTileSmall = 64;
