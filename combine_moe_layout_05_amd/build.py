@@ -39,6 +39,13 @@ HIPCC_FLAGS = [
     # is contracted, and fp32 denormals are kept (IEEE).
     "-ffp-contract=off",
     "-fno-gpu-flush-denormals-to-zero",
+    # Kernel arguments preloaded into SGPRs when a wavefront starts (gfx950),
+    # instead of each wavefront's first scalar load of them. Measured on
+    # MI355X, per step, four interleaved runs of 200 steps: 180.6-180.7
+    # against 181.0-181.3 us at 4096 tokens of 7168, 212.3-212.5 against
+    # 213.0-213.6 us at 8192 tokens of 4096, 32.3-32.4 against 32.7 us at
+    # 2047 tokens of 2048 (the layout gains most, 0.3-0.6 us).
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]
@@ -93,16 +100,6 @@ def _build_library(sources, out_path: str, verbose: bool) -> str:
         raise RuntimeError(f"hipcc link failed with status {res.returncode}")
     os.replace(tmp, out_path)
     return out_path
-
-
-def is_stale() -> bool:
-    for lib, sources in ((LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)):
-        if not os.path.exists(lib):
-            return True
-        t = os.path.getmtime(lib)
-        if any(os.path.getmtime(p) > t for p in [os.path.join(CSRC, s) for s in sources] + HEADERS):
-            return True
-    return False
 
 
 if __name__ == "__main__":
